@@ -1,0 +1,218 @@
+"""Benchmark: split-KV attention forward on one MI355X.
+
+Workload: the long-context packed-varlen prefill (one sequence, H = 12,
+Sq = 4096, Sk = 42700, D_qk = 192, D_v = 128, split_kv = 3, non-causal, bf16
+inputs N(0, 1) from a seeded generator, scale 1/sqrt(192)).  A step is the
+whole path: sk_valid_split_counts -> sk_attn_partial -> sk_attn_combine, with
+inputs already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (% bf16 MFMA peak) at Sq4096 Sk42700 H12; combine GB/s"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_hbm_traffic.json")
+PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/sk_common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in PARTIAL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(launch_units: float):
+    """HBM bytes per launch of the partial kernel from the committed rocprofv3
+    counter summary, or None when absent or taken on different kernel code."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, budget_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    the full split method (counts, partials, merge) for chunks of query rows
+    over all heads and all 42700 keys, until `budget_s` of wall time."""
+    import numpy as np
+
+    from oracle import adapter
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    host = {k: v.cpu() for k, v in inputs.items()}
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.sq[0])
+    done = 0
+    chunk = 32
+    t0 = time.perf_counter()
+    while done < len(order) and time.perf_counter() - t0 < budget_s:
+        rows = np.sort(order[done : done + chunk])
+        adapter.expected(w, host, 128, rows_per_seq={0: rows})
+        done += len(rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * (w.d_qk + w.d_v) * w.heads * done * w.sk[0]
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {w.sq[0]} query rows x {w.heads} heads x {w.sk[0]} keys (full method, f64, "
+                  f"{dt:.1f} s on {platform.processor() or platform.machine()})",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-iters", type=int, default=10, help="combine timings after a cache flush")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from split_kv_attention_amd import _lib, attention, workloads
+
+    w = workloads.LONG_PREFILL
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inputs = workloads.make_inputs(w, dev, seed=3)
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+    counts, o_part, lse_part, out, lse_out = attention.alloc_outputs(prob, inputs["q"], inputs["v"])
+    q, k, v = inputs["q"], inputs["k"], inputs["v"]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        _lib.sk_valid_split_counts(prob.c, counts, sh)
+        if ev:
+            ev[1].record(stream)
+        _lib.sk_attn_partial(prob.c, q, k, v, o_part, lse_part, sh)
+        if ev:
+            ev[2].record(stream)
+        _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    t_counts = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_partial = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_combine = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    # combine after evicting L2 and the 256 MB infinity cache
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_iters):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
+    del flush
+
+    H, Sq, Sk, S = w.heads, w.sq[0], w.sk[0], w.split_kv
+    flops = 2.0 * (w.d_qk + w.d_v) * H * Sq * Sk  # non-causal: every (query, key) pair is visible
+    rows = Sq
+    combine_bytes = (S * H * rows * w.d_v * 4 + S * H * rows * 4 + rows * 4 + rows * H * w.d_v * 2 + H * rows * 4)
+    partial_bytes = (rows * H * w.d_qk * 2 + Sk * H * (w.d_qk + w.d_v) * 2 + S * H * rows * (w.d_v + 1) * 4)
+    achieved = flops / (t_partial * 1e-3) / 1e12
+    traffic = measured_traffic(1)
+    res = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16 inputs from a seeded generator",
+        "config": {
+            "workload": w.name,
+            "batch": 1, "heads": H, "seqlen_q": Sq, "seqlen_k": Sk, "d_qk": w.d_qk, "d_v": w.d_v,
+            "split_kv": S, "n_per_block": w.n_per_block, "mask": w.mask, "layout": "packed varlen",
+            "m_per_block": prob.m_per_block,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "kernel": "partial_bf16_kernel<192,128>",
+            "kernel_ms": t_partial,
+            "algorithmic_flop": flops,
+            "algorithmic_bytes": partial_bytes,
+        },
+        "combine": {
+            "bound": "hbm",
+            "ms_in_pipeline": t_combine,
+            "ms_cold_cache": t_combine_cold,
+            "algorithmic_bytes": combine_bytes,
+            "gbps_in_pipeline": combine_bytes / (t_combine * 1e-3) / 1e9,
+            "gbps_cold_cache": combine_bytes / (t_combine_cold * 1e-3) / 1e9,
+            "frac_cold_cache": combine_bytes / (t_combine_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "peak": PEAK_HBM_GBPS,
+        },
+        "counts_ms": t_counts,
+        "attention_tflops_partial_plus_combine": flops / ((t_partial + t_combine) * 1e-3) / 1e12,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inputs)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,169 @@
+/*
+ * libsplitkv: split-KV attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * The key axis of every (sequence, head) is divided into split_kv chunks.
+ * sk_attn_partial computes one partial output O_s and one log-sum-exp L_s per
+ * chunk; sk_attn_combine merges them into the attention output with the
+ * NaN-safe f32 rule; sk_valid_split_counts gives the per-row number of splits
+ * the merge reads.  The method is the one described on the page "Recombine
+ * fully masked split-KV attention partials on the host" (rocmlirTriton pull
+ * request #535); the packed variable-length batch and the num_splits knob
+ * follow "[ASM][HIP][JIT][gfx942] Optimize long-context FMHA with split-KV"
+ * (aiter pull request #5592).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates, frees and synchronises nothing; it only enqueues
+ *     kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream).  Calls are asynchronous and thread-safe.
+ *   - Arguments are checked on the host before anything is enqueued.  An
+ *     invalid argument returns SK_ERR_INVALID_ARG, a valid request this
+ *     build does not implement returns SK_ERR_UNSUPPORTED, and a failed
+ *     launch returns SK_ERR_HIP; sk_last_error() then holds a message for the
+ *     calling thread.  Nothing is written to device memory on error.
+ *   - Device arrays named in sk_problem (cu_seqlens, per-sequence values) are
+ *     read by the kernels; the host never dereferences them, so their values
+ *     cannot be checked before launch.  They must be consistent with the
+ *     scalar fields (see each field).
+ *
+ * Row numbering.  "Rows" are the packed query rows of the whole batch: with
+ * cu_seqlens_q the row of (sequence b, query r) is cu_seqlens_q[b] + r; without
+ * it (dense batch) it is b * max_seqlen_q + r.  sk_rows() returns their number.
+ *
+ * Partial buffers (written by sk_attn_partial, read by sk_attn_combine), f32:
+ *   o_part   [num_heads][split_kv][rows][head_dim_v]
+ *   lse_part [num_heads][split_kv][rows]
+ * i.e. the split axis sits right after the batch-head axis, as in the per-row
+ * mask layout of the rocmlirTriton page ("Per-row mask layout").
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SK_ABI_VERSION 1
+
+typedef enum sk_status {
+    SK_OK = 0,
+    SK_ERR_INVALID_ARG = 1,
+    SK_ERR_UNSUPPORTED = 2,
+    SK_ERR_HIP = 3
+} sk_status;
+
+/* Key visibility of query row q of a sequence with lastValid as below:
+ *   NONE           keys 0 .. lastValid
+ *   CAUSAL         keys 0 .. min(q, lastValid)                (top-left aligned)
+ *   PREFIX_CAUSAL  keys 0 .. min(q + prefix_offset, lastValid)
+ * (rocmlirTriton page, "Per-row valid-split counts": prefix_offset is 0 for
+ * plain causal).  A row that sees no key is fully masked: output 0, LSE -inf. */
+typedef enum sk_mask_mode {
+    SK_MASK_NONE = 0,
+    SK_MASK_CAUSAL = 1,
+    SK_MASK_PREFIX_CAUSAL = 2
+} sk_mask_mode;
+
+typedef enum sk_dtype {
+    SK_F32 = 0,
+    SK_BF16 = 1
+} sk_dtype;
+
+typedef struct sk_problem {
+    int32_t batch;          /* B >= 0: number of sequences */
+    int32_t num_heads;      /* H >= 1 (query, key and value heads are equal) */
+    int32_t max_seqlen_q;   /* dense: every Sq_b; varlen: >= every Sq_b */
+    int32_t max_seqlen_k;   /* dense: every Sk_b; varlen: >= every Sk_b */
+    int32_t total_q;        /* varlen (cu_seqlens_q != NULL): rows of Q / out,
+                               = cu_seqlens_q[B]; ignored for a dense batch */
+    int32_t head_dim_qk;    /* D_qk */
+    int32_t head_dim_v;     /* D_v */
+    int32_t split_kv;       /* S_max >= 1: splits per (sequence, head); 1 = unsplit
+                               (aiter page: num_splits 2..8 force a split) */
+    int32_t n_per_block;    /* split granularity in keys (>= 1): the key tile
+                               nPerBlock of the count formula */
+    int32_t mask;           /* sk_mask_mode */
+    int32_t dtype;          /* sk_dtype of Q, K, V */
+    int32_t out_dtype;      /* sk_dtype of out */
+    int64_t prefix_offset;  /* PREFIX_CAUSAL only (may be negative) */
+    int64_t last_valid_kv_index; /* < 0: Sk_b - 1; otherwise min(value, Sk_b - 1) */
+    float softmax_scale;    /* > 0, finite: scores are scale * q.k */
+    int32_t reserved0;      /* must be 0 */
+    const int32_t* cu_seqlens_q;          /* device [B+1] prefix sums, or NULL = dense */
+    const int32_t* cu_seqlens_k;          /* device [B+1] prefix sums, or NULL = dense */
+    const int32_t* split_kv_per_seq;      /* device [B], each in 1..split_kv, or NULL */
+    const int32_t* prefix_offset_per_seq; /* device [B] (PREFIX_CAUSAL), or NULL */
+    const int32_t* last_valid_per_seq;    /* device [B] (< 0: Sk_b - 1), or NULL */
+    /* Element strides.  The head dimension is contiguous (stride 1).  The batch
+     * stride of a tensor is used only when its cu_seqlens pointer is NULL. */
+    int64_t q_stride_row, q_stride_head, q_stride_batch;
+    int64_t k_stride_row, k_stride_head, k_stride_batch;
+    int64_t v_stride_row, v_stride_head, v_stride_batch;
+    int64_t o_stride_row, o_stride_head, o_stride_batch;
+} sk_problem;
+
+/* ABI version of the library (SK_ABI_VERSION of the header it was built from). */
+int32_t sk_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sk_last_error(void);
+
+/* Human-readable name of a status code. */
+const char* sk_status_string(sk_status status);
+
+/* Number of packed query rows (see "Row numbering"), or -1 if `p` is invalid. */
+int64_t sk_rows(const sk_problem* p);
+
+/* Bytes of the partial buffers sk_attn_partial writes and sk_attn_combine
+ * reads (layout in the file header).  Either output pointer may be NULL. */
+sk_status sk_workspace_bytes(const sk_problem* p, size_t* o_part_bytes, size_t* lse_part_bytes);
+
+/* Query rows per M block of the partial kernel selected for `p` (>= 1), or -1
+ * if `p` is invalid or unsupported.  The kernel partitions each block's keys
+ * with the count formula evaluated at the block's last row (rocmlirTriton
+ * page, the paragraph on conservative counts), so the partials depend on it. */
+int32_t sk_partial_m_per_block(const sk_problem* p);
+
+/* Per-row valid-split counts (rocmlirTriton page, "Per-row valid-split
+ * counts"):
+ *   rowLast      = max(0, vis(q))  with vis(q) the row's last visible key
+ *   keysPerSplit = nPerBlock * ceil(ceil((rowLast + 1) / nPerBlock) / S_b)
+ *   count        = ceil((rowLast + 1) / keysPerSplit)
+ * counts: device int32 [rows], written for every row of every sequence
+ * (1 <= count <= S_b).  The count is head-independent. */
+sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stream);
+
+/* Per-split partial attention (rocmlirTriton page, Summary).  For every
+ * sequence b, head h, split s < S_b and row: O_s and L_s (natural-log LSE of
+ * the scaled scores) of softmax attention over the keys of split s of the
+ * row's M block that the row may see.  Split s of a block covers keys
+ * [s*kps, min((s+1)*kps, rowLast_blk + 1)) with kps the keys-per-split of the
+ * block's last row.  A split with no such key writes O_s = 0, L_s = -inf.
+ * Every (h, s < S_b, row) slot is written, so the buffers need no clearing.
+ * q, k, v: device, dtype; o_part, lse_part: device f32, layout in the header,
+ * at least sk_workspace_bytes() bytes. */
+sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v,
+                          float* o_part, float* lse_part, void* stream);
+
+/* NaN-safe f32 merge of the partials (rocmlirTriton page, "NaN-safe merge" and
+ * "f32 merge for f16/bf16"), per (row, head) with c = count of the row:
+ *   m   = max(max_{s<c} L_s, lowest finite f32)
+ *   w_s = exp(L_s - m)
+ *   O   = sum_{s<c} w_s O_s / max(sum_{s<c} w_s, 1)      (cast to out_dtype last)
+ *   LSE = m + ln(sum_{s<c} w_s), or -inf when the sum is 0
+ * Splits s >= c are never read.  counts: device int32 [rows] from
+ * sk_valid_split_counts, or NULL to evaluate the same formula inline.
+ * out: device out_dtype with the o_stride_* layout, fully overwritten (a fully
+ * masked row becomes 0).  lse_out: device f32 [num_heads][rows], or NULL to
+ * skip it (the aiter page's return_lse=False). */
+sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float* lse_part,
+                          const int32_t* counts, void* out, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_H */

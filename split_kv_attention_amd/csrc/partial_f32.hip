@@ -1,0 +1,166 @@
+// Split-KV partial attention, f32 storage and f32 arithmetic (VALU).
+//
+// Computes, per (sequence, head, split, query block), the partial output O_s
+// and log-sum-exp L_s of softmax attention over the split's keys, the method
+// of the rocmlirTriton page "Recombine fully masked split-KV attention
+// partials on the host" (Summary; the block partition in "Per-row valid-split
+// counts").  gfx950 has no reduced-precision f32 matrix path that would keep
+// an f32 problem at f32 accuracy, so this variant uses FMA on the vector ALUs:
+// one lane per query row, key/value tiles staged through LDS and read as
+// wave-wide broadcasts.  It serves small f32 problems; bf16 goes to MFMA.
+#include "sk_common.hpp"
+
+namespace sk {
+
+namespace {
+
+constexpr int kF32Rows = 64;  // query rows per workgroup (one wave)
+
+template <int DQK, int DV, int BN>
+__global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
+    __shared__ float4 Ks[BN * DQK / 4];
+    __shared__ float4 Vs[BN * DV / 4];
+
+    const WorkItem it = decode_work(a);
+    const Seq sq = load_seq(a.seqs, it.batch);
+    if (it.split >= sq.splits) return;
+    const int r0 = it.tile * kF32Rows;
+    if (r0 >= sq.sq) return;
+    const int mask = a.seqs.mask;
+
+    // Key range of this split for this block: the count formula at the
+    // block's last row decides keys per split.
+    const int last_row = min(r0 + kF32Rows, sq.sq) - 1;
+    const int64_t rl = row_last(sq, mask, last_row);
+    const int64_t kps = keys_per_split(rl, a.seqs.n_per_block, sq.splits);
+    // Split s covers [s*kps, (s+1)*kps) of the keys 0..rowLast.  Keys past
+    // lastValid are never visible, so an empty key range (lastValid = -1)
+    // gives an empty loop and no key is loaded.
+    const int64_t kend = min(rl + 1, sq.lv + 1);
+    const int ks = (int)min((int64_t)it.split * kps, kend);
+    const int ke = (int)min((int64_t)(it.split + 1) * kps, kend);
+
+    const int lane = threadIdx.x;
+    const int qrow = r0 + lane;
+    const bool row_ok = qrow < sq.sq;
+    const int64_t vis = vis_last(sq, mask, qrow);
+
+    const float* qp = reinterpret_cast<const float*>(a.q) +
+                      (a.seqs.cu_q ? (sq.row0 + qrow) * a.q_row : (int64_t)it.batch * a.q_batch + (int64_t)qrow * a.q_row) +
+                      (int64_t)it.head * a.q_head;
+    const float* kp = reinterpret_cast<const float*>(a.k) +
+                      (sq.krow0 >= 0 ? sq.krow0 * a.k_row : (int64_t)it.batch * a.k_batch) + (int64_t)it.head * a.k_head;
+    const float* vp = reinterpret_cast<const float*>(a.v) +
+                      (sq.krow0 >= 0 ? sq.krow0 * a.v_row : (int64_t)it.batch * a.v_batch) + (int64_t)it.head * a.v_head;
+
+    float qv[DQK];
+#pragma unroll
+    for (int d = 0; d < DQK; d += 4) {
+        float4 x = row_ok ? *reinterpret_cast<const float4*>(qp + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[d] = x.x;
+        qv[d + 1] = x.y;
+        qv[d + 2] = x.z;
+        qv[d + 3] = x.w;
+    }
+    float o[DV];
+#pragma unroll
+    for (int d = 0; d < DV; ++d) o[d] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float c = a.scale_log2;
+
+    for (int kt = ks; kt < ke; kt += BN) {
+        __syncthreads();
+        for (int i = lane; i < BN * DQK / 4; i += kF32Rows) {
+            const int kr = i / (DQK / 4), col = i % (DQK / 4);
+            const int key = kt + kr;
+            Ks[i] = key < ke ? *reinterpret_cast<const float4*>(kp + (int64_t)key * a.k_row + col * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int i = lane; i < BN * DV / 4; i += kF32Rows) {
+            const int kr = i / (DV / 4), col = i % (DV / 4);
+            const int key = kt + kr;
+            Vs[i] = key < ke ? *reinterpret_cast<const float4*>(vp + (int64_t)key * a.v_row + col * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        __syncthreads();
+
+        float sc[BN];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int d = 0; d < DQK / 4; ++d) {
+                const float4 kk = Ks[j * (DQK / 4) + d];
+                dot = fmaf(qv[4 * d], kk.x, dot);
+                dot = fmaf(qv[4 * d + 1], kk.y, dot);
+                dot = fmaf(qv[4 * d + 2], kk.z, dot);
+                dot = fmaf(qv[4 * d + 3], kk.w, dot);
+            }
+            const int key = kt + j;
+            sc[j] = (key < ke && key <= vis) ? dot : -INFINITY;
+            mx = fmaxf(mx, sc[j]);
+        }
+        // Online softmax in base 2; a row with nothing visible yet keeps
+        // m = -inf and zero weights (no -inf - -inf).
+        const float m_new = fmaxf(m, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f((m - m_use) * c);
+        const float mc = m_use * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            sc[j] = exp2f(fmaf(sc[j], c, -mc));
+            rs += sc[j];
+        }
+        l = fmaf(l, alpha, rs);
+        m = m_new;
+#pragma unroll
+        for (int d = 0; d < DV / 4; ++d) {
+            float4 acc = make_float4(o[4 * d] * alpha, o[4 * d + 1] * alpha, o[4 * d + 2] * alpha, o[4 * d + 3] * alpha);
+#pragma unroll
+            for (int j = 0; j < BN; ++j) {
+                const float4 vv = Vs[j * (DV / 4) + d];
+                acc.x = fmaf(sc[j], vv.x, acc.x);
+                acc.y = fmaf(sc[j], vv.y, acc.y);
+                acc.z = fmaf(sc[j], vv.z, acc.z);
+                acc.w = fmaf(sc[j], vv.w, acc.w);
+            }
+            o[4 * d] = acc.x;
+            o[4 * d + 1] = acc.y;
+            o[4 * d + 2] = acc.z;
+            o[4 * d + 3] = acc.w;
+        }
+    }
+
+    if (!row_ok) return;
+    const int64_t prow = sq.row0 + qrow;
+    if (prow >= a.rows) return;
+    // Empty split or fully masked row: O_s = 0, L_s = -inf.
+    const bool empty = (m == -INFINITY);
+    const float inv = empty ? 0.f : 1.0f / l;
+    const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+    float* op = a.o_part + slot * DV;
+#pragma unroll
+    for (int d = 0; d < DV; d += 4)
+        *reinterpret_cast<float4*>(op + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
+    a.lse_part[slot] = empty ? -INFINITY : m * a.scale + logf(l);
+}
+
+template <int DQK, int DV, int BN>
+hipError_t launch(const PartialArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((partial_f32_kernel<DQK, DV, BN>), dim3(a.n_work), dim3(kF32Rows), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+PartialKernel find_partial_f32(int d_qk, int d_v) {
+    if (d_qk == 16 && d_v == 16) return {launch<16, 16, 32>, kF32Rows};
+    if (d_qk == 32 && d_v == 32) return {launch<32, 32, 32>, kF32Rows};
+    if (d_qk == 64 && d_v == 64) return {launch<64, 64, 32>, kF32Rows};
+    if (d_qk == 128 && d_v == 128) return {launch<128, 128, 16>, kF32Rows};
+    return {nullptr, 0};
+}
+
+}  // namespace sk

@@ -1,0 +1,245 @@
+// libsplitkv C ABI: argument checking and kernel dispatch.  Every check runs
+// on the host before anything is enqueued; the library never allocates,
+// frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sk_common.hpp"
+#include "splitkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kMaxSplits = 128;
+constexpr int kMaxHeadDim = 256;
+
+sk_status fail(sk_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sk_status fail(sk_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sk_status ok() {
+    g_last_error.clear();
+    return SK_OK;
+}
+
+int64_t rows_of(const sk_problem& p) {
+    return p.cu_seqlens_q ? (int64_t)p.total_q : (int64_t)p.batch * p.max_seqlen_q;
+}
+
+int elem_bytes(int dtype) { return dtype == SK_BF16 ? 2 : 4; }
+
+// Checks every scalar field.  Pointer checks depend on the entry point.
+sk_status check_problem(const sk_problem* p) {
+    if (!p) return fail(SK_ERR_INVALID_ARG, "problem is NULL");
+    if (p->batch < 0) return fail(SK_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", p->batch);
+    if (p->num_heads < 1) return fail(SK_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", p->num_heads);
+    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
+        return fail(SK_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0 (got %d, %d)", p->max_seqlen_q, p->max_seqlen_k);
+    if (p->cu_seqlens_q && p->total_q < 0) return fail(SK_ERR_INVALID_ARG, "total_q must be >= 0 (got %d)", p->total_q);
+    if (p->head_dim_qk < 1 || p->head_dim_v < 1)
+        return fail(SK_ERR_INVALID_ARG, "head dims must be >= 1 (got %d, %d)", p->head_dim_qk, p->head_dim_v);
+    if (p->head_dim_qk > kMaxHeadDim || p->head_dim_v > kMaxHeadDim)
+        return fail(SK_ERR_UNSUPPORTED, "head dims above %d are not supported (got %d, %d)", kMaxHeadDim,
+                    p->head_dim_qk, p->head_dim_v);
+    if (p->split_kv < 1) return fail(SK_ERR_INVALID_ARG, "split_kv must be >= 1 (got %d)", p->split_kv);
+    if (p->split_kv > kMaxSplits)
+        return fail(SK_ERR_UNSUPPORTED, "split_kv above %d is not supported (got %d)", kMaxSplits, p->split_kv);
+    if (p->n_per_block < 1) return fail(SK_ERR_INVALID_ARG, "n_per_block must be >= 1 (got %d)", p->n_per_block);
+    if (p->mask != SK_MASK_NONE && p->mask != SK_MASK_CAUSAL && p->mask != SK_MASK_PREFIX_CAUSAL)
+        return fail(SK_ERR_INVALID_ARG, "unknown mask mode %d", p->mask);
+    if (p->dtype != SK_F32 && p->dtype != SK_BF16) return fail(SK_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (p->out_dtype != SK_F32 && p->out_dtype != SK_BF16)
+        return fail(SK_ERR_INVALID_ARG, "unknown out_dtype %d", p->out_dtype);
+    if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
+        return fail(SK_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+    if (p->reserved0 != 0) return fail(SK_ERR_INVALID_ARG, "reserved0 must be 0");
+    const int64_t strides[] = {p->q_stride_row, p->q_stride_head, p->q_stride_batch, p->k_stride_row,
+                               p->k_stride_head, p->k_stride_batch, p->v_stride_row, p->v_stride_head,
+                               p->v_stride_batch, p->o_stride_row, p->o_stride_head, p->o_stride_batch};
+    for (int64_t s : strides)
+        if (s < 0) return fail(SK_ERR_INVALID_ARG, "strides must be >= 0");
+    if ((int64_t)p->max_seqlen_q * p->num_heads > (int64_t)1 << 40 || rows_of(*p) > (int64_t)1 << 31)
+        return fail(SK_ERR_UNSUPPORTED, "problem too large");
+    return SK_OK;
+}
+
+sk::SeqTable seq_table(const sk_problem& p) {
+    sk::SeqTable t;
+    t.cu_q = p.cu_seqlens_q;
+    t.cu_k = p.cu_seqlens_k;
+    t.splits = p.split_kv_per_seq;
+    t.offsets = p.prefix_offset_per_seq;
+    t.last_valid = p.last_valid_per_seq;
+    t.max_sq = p.max_seqlen_q;
+    t.max_sk = p.max_seqlen_k;
+    t.s_max = p.split_kv;
+    t.mask = p.mask;
+    t.n_per_block = p.n_per_block;
+    t.pad_ = 0;
+    t.prefix_offset = p.prefix_offset;
+    t.last_valid_kv_index = p.last_valid_kv_index;
+    return t;
+}
+
+bool aligned(const void* ptr, size_t bytes) { return ((uintptr_t)ptr % bytes) == 0; }
+
+sk::PartialKernel pick_partial(const sk_problem& p) {
+    return p.dtype == SK_BF16 ? sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v)
+                              : sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
+}
+
+sk_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sk_abi_version(void) { return SK_ABI_VERSION; }
+
+const char* sk_last_error(void) { return g_last_error.c_str(); }
+
+const char* sk_status_string(sk_status status) {
+    switch (status) {
+        case SK_OK: return "SK_OK";
+        case SK_ERR_INVALID_ARG: return "SK_ERR_INVALID_ARG";
+        case SK_ERR_UNSUPPORTED: return "SK_ERR_UNSUPPORTED";
+        case SK_ERR_HIP: return "SK_ERR_HIP";
+    }
+    return "SK_UNKNOWN_STATUS";
+}
+
+int64_t sk_rows(const sk_problem* p) {
+    if (check_problem(p) != SK_OK) return -1;
+    return rows_of(*p);
+}
+
+sk_status sk_workspace_bytes(const sk_problem* p, size_t* o_part_bytes, size_t* lse_part_bytes) {
+    sk_status st = check_problem(p);
+    if (st != SK_OK) return st;
+    const size_t slots = (size_t)p->num_heads * p->split_kv * (size_t)rows_of(*p);
+    if (o_part_bytes) *o_part_bytes = slots * p->head_dim_v * sizeof(float);
+    if (lse_part_bytes) *lse_part_bytes = slots * sizeof(float);
+    return ok();
+}
+
+int32_t sk_partial_m_per_block(const sk_problem* p) {
+    if (check_problem(p) != SK_OK) return -1;
+    const sk::PartialKernel k = pick_partial(*p);
+    if (!k.launch) {
+        fail(SK_ERR_UNSUPPORTED, "no partial kernel for dtype %d, head dims (%d, %d)", p->dtype, p->head_dim_qk,
+             p->head_dim_v);
+        return -1;
+    }
+    ok();
+    return k.m_per_block;
+}
+
+sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stream) {
+    sk_status st = check_problem(p);
+    if (st != SK_OK) return st;
+    if (p->batch == 0 || p->max_seqlen_q == 0 || rows_of(*p) == 0) return ok();
+    if (!counts) return fail(SK_ERR_INVALID_ARG, "counts is NULL");
+    sk::CountsArgs a;
+    a.counts = counts;
+    a.seqs = seq_table(*p);
+    return hip_status(sk::launch_counts(a, p->batch, (hipStream_t)stream), "counts kernel launch");
+}
+
+sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v, float* o_part,
+                          float* lse_part, void* stream) {
+    sk_status st = check_problem(p);
+    if (st != SK_OK) return st;
+    const sk::PartialKernel kern = pick_partial(*p);
+    if (!kern.launch)
+        return fail(SK_ERR_UNSUPPORTED, "no partial kernel for dtype %s with head dims (%d, %d)",
+                    p->dtype == SK_BF16 ? "bf16" : "f32", p->head_dim_qk, p->head_dim_v);
+    const int64_t rows = rows_of(*p);
+    if (p->batch == 0 || p->max_seqlen_q == 0 || rows == 0) return ok();
+    if (!q || !k || !v || !o_part || !lse_part) return fail(SK_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    // Vector loads: 16-byte rows of Q/K/V, 16-byte rows of o_part.
+    const int vec = 16 / elem_bytes(p->dtype);
+    const int64_t qkv_strides[] = {p->q_stride_row, p->q_stride_head, p->q_stride_batch,
+                                   p->k_stride_row, p->k_stride_head, p->k_stride_batch,
+                                   p->v_stride_row, p->v_stride_head, p->v_stride_batch};
+    for (int64_t s : qkv_strides)
+        if (s % vec) return fail(SK_ERR_UNSUPPORTED, "Q/K/V strides must be multiples of %d elements", vec);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+        return fail(SK_ERR_UNSUPPORTED, "Q/K/V/o_part must be 16-byte aligned");
+
+    const int64_t n_tiles = (p->max_seqlen_q + kern.m_per_block - 1) / kern.m_per_block;
+    const int64_t n_work = n_tiles * p->num_heads * p->split_kv * (int64_t)p->batch;
+    if (n_work >= ((int64_t)1 << 31)) return fail(SK_ERR_UNSUPPORTED, "too many work items");
+
+    sk::PartialArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.seqs = seq_table(*p);
+    a.q_row = p->q_stride_row;
+    a.q_head = p->q_stride_head;
+    a.q_batch = p->q_stride_batch;
+    a.k_row = p->k_stride_row;
+    a.k_head = p->k_stride_head;
+    a.k_batch = p->k_stride_batch;
+    a.v_row = p->v_stride_row;
+    a.v_head = p->v_stride_head;
+    a.v_batch = p->v_stride_batch;
+    a.rows = rows;
+    a.heads = p->num_heads;
+    a.n_tiles = (int32_t)n_tiles;
+    a.n_work = (uint32_t)n_work;
+    a.scale = p->softmax_scale;
+    a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    return hip_status(kern.launch(a, (hipStream_t)stream), "partial kernel launch");
+}
+
+sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float* lse_part, const int32_t* counts,
+                          void* out, float* lse_out, void* stream) {
+    sk_status st = check_problem(p);
+    if (st != SK_OK) return st;
+    const int64_t rows = rows_of(*p);
+    if (p->batch == 0 || p->max_seqlen_q == 0 || rows == 0) return ok();
+    if (!o_part || !lse_part || !out) return fail(SK_ERR_INVALID_ARG, "o_part, lse_part and out must not be NULL");
+    if (p->head_dim_v % 4) return fail(SK_ERR_UNSUPPORTED, "head_dim_v must be a multiple of 4");
+    const int64_t ostr[] = {p->o_stride_row, p->o_stride_head, p->o_stride_batch};
+    for (int64_t s : ostr)
+        if (s % 4) return fail(SK_ERR_UNSUPPORTED, "out strides must be multiples of 4 elements");
+    if (!aligned(out, 4 * elem_bytes(p->out_dtype)) || !aligned(o_part, 16))
+        return fail(SK_ERR_UNSUPPORTED, "out / o_part are not aligned for 4-element vectors");
+    if ((int64_t)p->max_seqlen_q * p->num_heads * (p->head_dim_v / 4) >= ((int64_t)1 << 31) * 256)
+        return fail(SK_ERR_UNSUPPORTED, "problem too large for the combine grid");
+    sk::CombineArgs a;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.counts = counts;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.seqs = seq_table(*p);
+    a.o_row = p->o_stride_row;
+    a.o_head = p->o_stride_head;
+    a.o_batch = p->o_stride_batch;
+    a.rows = rows;
+    a.heads = p->num_heads;
+    a.dv = p->head_dim_v;
+    return hip_status(sk::launch_combine(a, p->batch, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
+}
+
+}  // extern "C"
