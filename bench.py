@@ -93,6 +93,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10, help="combine timings after a cache flush")
+    ap.add_argument("--copy-check", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
@@ -155,6 +157,15 @@ def main() -> int:
     torch.cuda.synchronize()
     t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
     del flush
+
+    if args.copy_check:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.zero_()
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     H, Sq, Sk, S = w.heads, w.sq[0], w.sk[0], w.split_kv
     flops = 2.0 * (w.d_qk + w.d_v) * H * Sq * Sk  # non-causal: every (query, key) pair is visible

@@ -46,7 +46,7 @@ struct Cfg {
     static constexpr int K_CHUNKS = kBN * DQK / 8;      // 16-byte chunks of a K tile
     static constexpr int V_CHUNKS = (kBN / 4) * (DV / 8);  // (4 keys x 8 values) chunks of a V tile
     static constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
-    static constexpr int V_PER_T = (V_CHUNKS + kThreads - 1) / kThreads;
+    static_assert(V_CHUNKS <= kThreads, "one V chunk per thread at most");
     static constexpr int LDS_ELEMS = kBN * KS + DV * VS;
     static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must be multiples of 16 (QK) and 32 (V)");
 };
@@ -54,8 +54,15 @@ struct Cfg {
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
+// Growth of the running max (in log2 units) tolerated before the output
+// accumulator is rescaled.  Using a stale max m' <= m only changes the common
+// factor 2^(m - m') of every weight and of their sum, so O = sum p V / sum p
+// and LSE = m' + log(sum p) are unchanged; weights stay below 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void partial_bf16_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void partial_bf16_kernel(PartialArgs a) {
     using C = Cfg<DQK, DV>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
     uint16_t* Ks = smem;                 // [kBN][KS]
@@ -90,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void partial_bf16_kernel(PartialArgs a) {
     const int qrow = r0 + wave * 32 + col;
     const bool row_ok = qrow < sq.sq;
     const bool wave_active = (r0 + wave * 32) < sq.sq;
-    const int64_t vis_q = vis_last(sq, mask, qrow);
+    // Visibility limit of this lane's row, clamped into int range (keys are int).
+    const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
 
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) +
                             (sq.krow0 >= 0 ? sq.krow0 * a.k_row : (int64_t)it.batch * a.k_batch) +
@@ -117,67 +125,69 @@ __global__ __launch_bounds__(kThreads) void partial_bf16_kernel(PartialArgs a) {
 #pragma unroll
     for (int c = 0; c < DV / 32; ++c)
         for (int j = 0; j < 16; ++j) o[c][j] = 0.f;
-    float m_i = -INFINITY;  // running max of raw scores (this lane's query)
-    float l_i = 0.f;        // running sum of weights over this half-wave's keys
+    float m_i = -INFINITY;  // reference max of raw scores (this lane's query)
+    float l_i = 0.f;        // sum of weights over this half-wave's keys
     const float cl2 = a.scale_log2;
 
-    // Register staging of the next tile.
+    // Per-thread load assignment, fixed for every tile: K chunk i is row
+    // kr[i], 8-element column kc[i]; V chunk is 4 keys (vq) x 8 values (vd).
+    const int k_row32 = (int)a.k_row, v_row32 = (int)a.v_row;
+    int kr[C::K_PER_T], kc[C::K_PER_T];
+#pragma unroll
+    for (int i = 0; i < C::K_PER_T; ++i) {
+        const int c = min(tid + i * kThreads, C::K_CHUNKS - 1);
+        kr[i] = c / (DQK / 8);
+        kc[i] = (c % (DQK / 8)) * 8;
+    }
+    const int vc = min(tid, C::V_CHUNKS - 1);
+    const int vq = vc % (kBN / 4), vd = vc / (kBN / 4);
+    const bool v_loader = tid < C::V_CHUNKS;
+
+    // Register staging of the next tile.  Rows past the split's end load the
+    // split's last key instead (valid memory, finite values): their scores are
+    // masked to -inf and their weights are 0.
     uint4 kreg[C::K_PER_T];
-    uint4 vreg[C::V_PER_T][4];
+    uint4 vreg[4];
     auto gload = [&](int kt) {
+        const uint16_t* kt_ptr = kbase + (int64_t)kt * a.k_row;
+        const uint16_t* vt_ptr = vbase + (int64_t)kt * a.v_row;
+        const int last = ke - 1 - kt;  // last loadable row of this tile
+        if (last >= kBN - 1) {
 #pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < C::K_CHUNKS) {
-                const int r = c / (DQK / 8), c8 = c % (DQK / 8);
-                const int key = kt + r;
-                kreg[i] = key < ke ? *reinterpret_cast<const uint4*>(kbase + (int64_t)key * a.k_row + c8 * 8)
-                                   : make_uint4(0, 0, 0, 0);
-            }
-        }
+            for (int i = 0; i < C::K_PER_T; ++i)
+                kreg[i] = *reinterpret_cast<const uint4*>(kt_ptr + kr[i] * k_row32 + kc[i]);
 #pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < C::V_CHUNKS) {
-                const int kq = c % (kBN / 4), d8 = c / (kBN / 4);
+            for (int j = 0; j < 4; ++j)
+                vreg[j] = *reinterpret_cast<const uint4*>(vt_ptr + (4 * vq + j) * v_row32 + vd * 8);
+        } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = kt + 4 * kq + j;
-                    vreg[i][j] = key < ke ? *reinterpret_cast<const uint4*>(vbase + (int64_t)key * a.v_row + d8 * 8)
-                                          : make_uint4(0, 0, 0, 0);
-                }
-            }
+            for (int i = 0; i < C::K_PER_T; ++i)
+                kreg[i] = *reinterpret_cast<const uint4*>(kt_ptr + min(kr[i], last) * k_row32 + kc[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                vreg[j] = *reinterpret_cast<const uint4*>(vt_ptr + min(4 * vq + j, last) * v_row32 + vd * 8);
         }
     };
     auto lstore = [&]() {
 #pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < C::K_CHUNKS) {
-                const int r = c / (DQK / 8), c8 = c % (DQK / 8);
-                *reinterpret_cast<uint4*>(Ks + r * C::KS + c8 * 8) = kreg[i];
-            }
-        }
+        for (int i = 0; i < C::K_PER_T; ++i)
+            if (C::K_CHUNKS % kThreads == 0 || tid + i * kThreads < C::K_CHUNKS)
+                *reinterpret_cast<uint4*>(Ks + kr[i] * C::KS + kc[i]) = kreg[i];
         // V^T: four keys of one value column become one 8-byte row segment.
+        if (v_loader) {
+            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
 #pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < C::V_CHUNKS) {
-                const int kq = c % (kBN / 4), d8 = c / (kBN / 4);
-                const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-                const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-                const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-                const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint2 lo, hi;
-                    lo.x = pack_lo(w0[e], w1[e]);
-                    lo.y = pack_lo(w2[e], w3[e]);
-                    hi.x = pack_hi(w0[e], w1[e]);
-                    hi.y = pack_hi(w2[e], w3[e]);
-                    *reinterpret_cast<uint2*>(Vt + (d8 * 8 + 2 * e) * C::VS + 4 * kq) = lo;
-                    *reinterpret_cast<uint2*>(Vt + (d8 * 8 + 2 * e + 1) * C::VS + 4 * kq) = hi;
-                }
+            for (int e = 0; e < 4; ++e) {
+                uint2 lo, hi;
+                lo.x = pack_lo(w0[e], w1[e]);
+                lo.y = pack_lo(w2[e], w3[e]);
+                hi.x = pack_hi(w0[e], w1[e]);
+                hi.y = pack_hi(w2[e], w3[e]);
+                *reinterpret_cast<uint2*>(Vt + (vd * 8 + 2 * e) * C::VS + 4 * vq) = lo;
+                *reinterpret_cast<uint2*>(Vt + (vd * 8 + 2 * e + 1) * C::VS + 4 * vq) = hi;
             }
         }
     };
@@ -207,13 +217,12 @@ __global__ __launch_bounds__(kThreads) void partial_bf16_kernel(PartialArgs a) {
             //   kt + 32*kb + 8*(j/4) + 4*half + (j%4)   for query column `col`.
             const bool full = (kt + kBN <= ke) && ((int64_t)kt + kBN - 1 <= vis_first);
             if (!full) {
+                const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = kt + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-                        if (key >= ke || (int64_t)key > vis_q) sacc[kb][j] = -INFINITY;
-                    }
+                    for (int j = 0; j < 16; ++j)
+                        if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -221,29 +230,38 @@ __global__ __launch_bounds__(kThreads) void partial_bf16_kernel(PartialArgs a) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_i, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m_i - m_use) * cl2);
-            const float mc = m_use * cl2;
+            // Move the reference max only when it grew by more than the
+            // threshold for some row of the wave (rare after the first tiles).
+            const float m_cand = fmaxf(m_i, mx);
+            const bool grow = (m_cand - m_i) * cl2 > kRescaleThreshold;  // false while nothing is visible
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? m_cand : m_i;
+                const float alpha = grow ? __builtin_amdgcn_exp2f((m_i - m_new) * cl2) : 1.0f;
+                l_i *= alpha;
+#pragma unroll
+                for (int c = 0; c < DV / 32; ++c)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
+                m_i = m_new;
+            }
+            const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
 
             // P (rounded to bf16) in the B-operand layout of GEMM1; the row
-            // sum uses the rounded weights so O is a true weighted mean.
+            // sum adds the rounded weights, so O is their exact weighted mean.
             bf16x8 pf[2][2];
-            float rs = 0.f;
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
-                    pf[kb][j >> 3][j & 7] = p;
-                    rs += (float)p;
+                for (int j = 0; j < 16; j += 2) {
+                    bf16x2 p2;
+                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
+                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], cl2, -mc));
+                    pf[kb][j >> 3][j & 7] = p2[0];
+                    pf[kb][j >> 3][(j & 7) + 1] = p2[1];
+                    l_i = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_i, false);
                 }
-            l_i = fmaf(l_i, alpha, rs);
-            m_i = m_new;
-#pragma unroll
-            for (int c = 0; c < DV / 32; ++c)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
 
             // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
             // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4,
