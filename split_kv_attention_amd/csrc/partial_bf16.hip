@@ -17,15 +17,20 @@
 //    two half-waves.
 //  * The same accumulator layout is exactly the B operand layout (key-major,
 //    query column per lane) GEMM1 needs for O^T = V^T P^T, so P never leaves
-//    registers: it is rounded to bf16 in place.  V is the A operand and is
-//    staged transposed (V^T, key-contiguous) in LDS.
+//    registers: it is rounded to bf16 in place.  V stays row-major in LDS and
+//    its A operand is read with ds_read_b64_tr_b16, which hands each lane four
+//    keys of one value column.
+//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+//    register staging), double-buffered: the next tile streams in while the
+//    current one is multiplied, with one barrier per tile.  16-byte chunks are
+//    XOR-swizzled by row so both operand reads are bank-conflict free.
 //  * Online softmax in base 2 with the scale folded into one FMA per score;
-//    a row with no visible key so far keeps m = -inf and zero weights.
-//  * K rows are padded by 16 bytes and V^T rows by 8 bytes in LDS so that the
-//    128-bit and 64-bit operand reads are bank-conflict free.
-//  * Next key tile is prefetched into registers while the current one is
-//    multiplied; work items are remapped so each XCD streams one (head, split)
-//    key range through its own L2.
+//    the reference max moves only when it grows by more than 2^8, and a row
+//    with no visible key so far keeps m = -inf and zero weights.
+//  * Work items are remapped so each XCD streams one (head, split) key range
+//    through its own L2.
+#include <type_traits>
+
 #include "sk_common.hpp"
 
 namespace sk {
@@ -39,20 +44,60 @@ constexpr int kBM = 128;    // query rows per workgroup
 constexpr int kBN = 64;     // keys per tile
 constexpr int kThreads = 256;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int DQK, int DV>
 struct Cfg {
-    static constexpr int KS = DQK + 8;                  // K row stride in LDS (bf16)
-    static constexpr int VS = kBN + 4;                  // V^T row stride in LDS (bf16)
-    static constexpr int K_CHUNKS = kBN * DQK / 8;      // 16-byte chunks of a K tile
-    static constexpr int V_CHUNKS = (kBN / 4) * (DV / 8);  // (4 keys x 8 values) chunks of a V tile
-    static constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
-    static_assert(V_CHUNKS <= kThreads, "one V chunk per thread at most");
-    static constexpr int LDS_ELEMS = kBN * KS + DV * VS;
-    static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must be multiples of 16 (QK) and 32 (V)");
+    static constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
+    static constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
+    static constexpr int K_ELEMS = kBN * DQK;           // one K tile (bf16 elements)
+    static constexpr int V_ELEMS = kBN * DV;            // one V tile
+    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int K_LOADS = kBN * KCH / kThreads;  // 16-byte loads per thread per tile
+    static constexpr int V_LOADS = kBN * VCH / kThreads;
+    static constexpr int VG = (VCH / 4) < 4 ? (VCH / 4) : 4;  // V swizzle period (rows)
+    static_assert(DQK % 64 == 0 && DV % 32 == 0, "head dims must be multiples of 64 (QK) and 32 (V)");
+    static_assert((kBN * KCH) % kThreads == 0 && (kBN * VCH) % kThreads == 0, "whole loads per thread");
 };
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// LDS position (in 16-byte chunks within the row) of chunk c of K row r, and
+// of chunk q of V row r.  K: GEMM0 reads one chunk of 32 consecutive rows;
+// V: the transpose reads take 64 bytes of 4 consecutive rows.
+__device__ __forceinline__ int k_swz(int r, int c) { return c ^ (r & 7); }
+template <int VG>
+__device__ __forceinline__ int v_swz(int r, int q) { return q ^ (4 * (r % VG)); }
+
+__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// ds_read_b64_tr_b16 (gfx950): within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte rows addressed by lanes 4j + i / 4, j = 0..3.
+// Issued through asm so that the compiler does not hold it behind the
+// in-flight HBM -> LDS tile loads (they write the other buffer); the caller
+// waits on lgkmcnt explicitly before using the result (tr_wait).
+template <int OFS>
+__device__ __forceinline__ s16x4 tr_read(uint32_t addr) {
+    s16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFS));
+    return r;
+}
+
+// Waits until at most N LDS reads are outstanding; the operands tie the wait
+// to the registers those reads fill, so no use can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void tr_wait(s16x4 (&x)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+                 : "i"(N));
+}
 
 // Growth of the running max (in log2 units) tolerated before the output
 // accumulator is rescaled.  Using a stale max m' <= m only changes the common
@@ -64,9 +109,7 @@ template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void partial_bf16_kernel(PartialArgs a) {
     using C = Cfg<DQK, DV>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-    uint16_t* Ks = smem;                 // [kBN][KS]
-    uint16_t* Vt = smem + kBN * C::KS;   // [DV][VS]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF_ELEMS];
 
     const WorkItem it = decode_work(a);
     const Seq sq = load_seq(a.seqs, it.batch);
@@ -129,75 +172,59 @@ void partial_bf16_kernel(PartialArgs a) {
     float l_i = 0.f;        // sum of weights over this half-wave's keys
     const float cl2 = a.scale_log2;
 
-    // Per-thread load assignment, fixed for every tile: K chunk i is row
-    // kr[i], 8-element column kc[i]; V chunk is 4 keys (vq) x 8 values (vd).
+    // Direct HBM -> LDS tile loads.  Load i of this thread fills LDS chunk
+    // P = 256 i + tid of the tile (a wave covers 64 consecutive chunks); the
+    // chunk holds row P / CH and, after the swizzle, column chunk c of that row.
     const int k_row32 = (int)a.k_row, v_row32 = (int)a.v_row;
-    int kr[C::K_PER_T], kc[C::K_PER_T];
+    int k_r[C::K_LOADS], k_c[C::K_LOADS], v_r[C::V_LOADS], v_c[C::V_LOADS];
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-        const int c = min(tid + i * kThreads, C::K_CHUNKS - 1);
-        kr[i] = c / (DQK / 8);
-        kc[i] = (c % (DQK / 8)) * 8;
+    for (int i = 0; i < C::K_LOADS; ++i) {
+        const int P = i * kThreads + tid;
+        k_r[i] = P / C::KCH;
+        k_c[i] = k_swz(k_r[i], P % C::KCH) * 8;
     }
-    const int vc = min(tid, C::V_CHUNKS - 1);
-    const int vq = vc % (kBN / 4), vd = vc / (kBN / 4);
-    const bool v_loader = tid < C::V_CHUNKS;
-
-    // Register staging of the next tile.  Rows past the split's end load the
-    // split's last key instead (valid memory, finite values): their scores are
-    // masked to -inf and their weights are 0.
-    uint4 kreg[C::K_PER_T];
-    uint4 vreg[4];
-    auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::V_LOADS; ++i) {
+        const int P = i * kThreads + tid;
+        v_r[i] = P / C::VCH;
+        v_c[i] = v_swz<C::VG>(v_r[i], P % C::VCH) * 8;
+    }
+    // Rows past the split's end load the split's last key instead (valid
+    // memory, finite values): their scores are masked to -inf, weights 0.
+    auto issue = [&](int kt, uint16_t* buf) {
         const uint16_t* kt_ptr = kbase + (int64_t)kt * a.k_row;
         const uint16_t* vt_ptr = vbase + (int64_t)kt * a.v_row;
-        const int last = ke - 1 - kt;  // last loadable row of this tile
-        if (last >= kBN - 1) {
+        const int last = min(ke - 1 - kt, kBN - 1);
 #pragma unroll
-            for (int i = 0; i < C::K_PER_T; ++i)
-                kreg[i] = *reinterpret_cast<const uint4*>(kt_ptr + kr[i] * k_row32 + kc[i]);
+        for (int i = 0; i < C::K_LOADS; ++i)
+            load_lds16(kt_ptr + min(k_r[i], last) * k_row32 + k_c[i], buf + (i * kThreads + wave * 64) * 8);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vreg[j] = *reinterpret_cast<const uint4*>(vt_ptr + (4 * vq + j) * v_row32 + vd * 8);
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::K_PER_T; ++i)
-                kreg[i] = *reinterpret_cast<const uint4*>(kt_ptr + min(kr[i], last) * k_row32 + kc[i]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vreg[j] = *reinterpret_cast<const uint4*>(vt_ptr + min(4 * vq + j, last) * v_row32 + vd * 8);
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i)
-            if (C::K_CHUNKS % kThreads == 0 || tid + i * kThreads < C::K_CHUNKS)
-                *reinterpret_cast<uint4*>(Ks + kr[i] * C::KS + kc[i]) = kreg[i];
-        // V^T: four keys of one value column become one 8-byte row segment.
-        if (v_loader) {
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint2 lo, hi;
-                lo.x = pack_lo(w0[e], w1[e]);
-                lo.y = pack_lo(w2[e], w3[e]);
-                hi.x = pack_hi(w0[e], w1[e]);
-                hi.y = pack_hi(w2[e], w3[e]);
-                *reinterpret_cast<uint2*>(Vt + (vd * 8 + 2 * e) * C::VS + 4 * vq) = lo;
-                *reinterpret_cast<uint2*>(Vt + (vd * 8 + 2 * e + 1) * C::VS + 4 * vq) = hi;
-            }
-        }
+        for (int i = 0; i < C::V_LOADS; ++i)
+            load_lds16(vt_ptr + min(v_r[i], last) * v_row32 + v_c[i],
+                       buf + C::K_ELEMS + (i * kThreads + wave * 64) * 8);
     };
 
-    if (ks < ke) gload(ks);
+    // Per-lane LDS read offsets (elements).  GEMM0: K row kb*32 + col, chunk
+    // 2t + half.  GEMM1 (transpose read): source lane s = lane % 16 of each
+    // 16-lane group addresses key (4h + s/4 [+8]) and value columns
+    // 32c + 16 g2 + 4 (s%4) .. +3, g2 = (lane / 16) % 2.
+    const int k_rd = col * DQK;
+    const int k_x = col & 7;
+    const int s16 = lane & 15;
+    const int g2 = (lane >> 4) & 1;
+    const int v_key = half * 4 + (s16 >> 2);
+    const int v_sw = 4 * ((s16 >> 2) % C::VG);
+    const int v_q = 2 * g2 + ((s16 & 3) >> 1);
+    const int v_in = (s16 & 1) * 4;
+
+    if (ks < ke) issue(ks, smem);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    int cur = 0;
     for (int kt = ks; kt < ke; kt += kBN) {
-        __syncthreads();  // every wave is done with the previous tile
-        lstore();
-        __syncthreads();
-        if (kt + kBN < ke) gload(kt + kBN);
+        uint16_t* Kb = smem + cur * C::BUF_ELEMS;
+        uint16_t* Vb = Kb + C::K_ELEMS;
+        if (kt + kBN < ke) issue(kt + kBN, smem + (cur ^ 1) * C::BUF_ELEMS);
 
         if (wave_active) {
             // GEMM0: S^T[key][query] for two 32-key blocks.
@@ -207,9 +234,10 @@ void partial_bf16_kernel(PartialArgs a) {
                 for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
 #pragma unroll
             for (int t = 0; t < DQK / 16; ++t) {
+                const int pos = ((2 * t + half) ^ k_x) * 8;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + col) * C::KS + t * 16 + half * 8);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * DQK + k_rd + pos);
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
                 }
             }
@@ -264,27 +292,52 @@ void partial_bf16_kernel(PartialArgs a) {
                 }
 
             // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
-            // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4,
-            // so the A operand takes two 4-key runs of one V^T row.
+            // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
+            // the two transpose reads give this lane's value column at keys
+            // 32kb + 16u + 4half + 0..3 and + 8..11.  Step n + 1's reads are
+            // issued before step n's MFMAs.
+            static_assert(DV == 128 || DV == 64, "GEMM1 read schedule covers D_v of 64 and 128");
+            uint32_t vaddr[DV / 32];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int c = 0; c < DV / 32; ++c) vaddr[c] = lds_addr(Vb + v_key * DV + (((4 * c + v_q) ^ v_sw) * 8) + v_in);
+            s16x4 xa[8], xb[8];
+            auto issue_step = [&](s16x4(&x)[8], auto kb_c, auto u_c) {
+                constexpr int kb = decltype(kb_c)::value, u = decltype(u_c)::value;
+                constexpr int o0 = (kb * 32 + u * 16) * DV * 2, o1 = o0 + 8 * DV * 2;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int kofs = kb * 32 + u * 16 + half * 4;
-#pragma unroll
-                    for (int c = 0; c < DV / 32; ++c) {
-                        const uint16_t* vr = Vt + (c * 32 + col) * C::VS + kofs;
-                        uint4 va;
-                        const uint2 x0 = *reinterpret_cast<const uint2*>(vr);
-                        const uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
-                        va.x = x0.x;
-                        va.y = x0.y;
-                        va.z = x1.x;
-                        va.w = x1.y;
-                        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pf[kb][u], o[c], 0, 0, 0);
-                    }
+                for (int c = 0; c < DV / 32; ++c) {
+                    x[2 * c] = tr_read<o0>(vaddr[c]);
+                    x[2 * c + 1] = tr_read<o1>(vaddr[c]);
                 }
+#pragma unroll
+                for (int c = DV / 32; c < 4; ++c) x[2 * c] = x[2 * c + 1] = s16x4{0, 0, 0, 0};
+            };
+            auto mma_step = [&](s16x4(&x)[8], const bf16x8& p) {
+#pragma unroll
+                for (int c = 0; c < DV / 32; ++c) {
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * c], x[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[c], 0, 0, 0);
+                }
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            constexpr int kReads = DV / 16;  // reads per step
+            issue_step(xa, I0{}, I0{});
+            issue_step(xb, I0{}, I1{});
+            tr_wait<kReads>(xa);
+            mma_step(xa, pf[0][0]);
+            issue_step(xa, I1{}, I0{});
+            tr_wait<kReads>(xb);
+            mma_step(xb, pf[0][1]);
+            issue_step(xb, I1{}, I1{});
+            tr_wait<kReads>(xa);
+            mma_step(xa, pf[1][0]);
+            tr_wait<0>(xb);
+            mma_step(xb, pf[1][1]);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of the next tile landed
+        __syncthreads();                     // all loads landed, every wave is done with `cur`
+        cur ^= 1;
     }
 
     if (!row_ok) return;
