@@ -90,6 +90,31 @@ __device__ __forceinline__ s16x4 tr_read(uint32_t addr) {
     return r;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b128 through asm, for the same reason as tr_read (GEMM0's K
+// fragments are read one step ahead of the MFMAs that use them).
+template <int OFS>
+__device__ __forceinline__ i32x4_t k_read(uint32_t addr) {
+    i32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFS));
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void k_wait(i32x4_t& a, i32x4_t& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// Value of lane l ^ 32 (the other half-wave).  v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second, so
+// with both = x the first result holds x[l - 32] in lanes 32..63 and the
+// second holds x[l + 32] in lanes 0..31.
+__device__ __forceinline__ float other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Waits until at most N LDS reads are outstanding; the operands tie the wait
 // to the registers those reads fill, so no use can be scheduled before it.
 template <int N>
@@ -217,123 +242,155 @@ void partial_bf16_kernel(PartialArgs a) {
     const int v_q = 2 * g2 + ((s16 & 3) >> 1);
     const int v_in = (s16 & 1) * 4;
 
+    // Tiles [ks, full_end) lie inside the split and below every row's limit.
+    const int64_t full_last = min((int64_t)ke - kBN, vis_first - (kBN - 1));  // last unmasked tile start
+    const int full_end = full_last < ks ? ks : (int)(ks + ((full_last - ks) / kBN + 1) * kBN);
+
+    // One key tile: GEMM0, softmax, GEMM1.  Tiles from full_end on (the
+    // ragged end of the split, or keys beyond some row's causal limit) are
+    // masked per element.
+    auto tile = [&](int kt, const uint16_t* Kb, const uint16_t* Vb) {
+        // GEMM0: S^T[key][query] for two 32-key blocks; K fragments for step
+        // t + 1 are read while step t multiplies.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
+        {
+            // per-lane bases: chunk (2(t%4) + half) ^ (col & 7); t/4 adds 128 bytes
+            uint32_t kaddr[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kaddr[m] = lds_addr(Kb + k_rd + (((2 * m + half) ^ k_x) * 8));
+            i32x4_t f[2][2];
+            auto rd = [&](i32x4_t(&x)[2], auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                x[0] = k_read<(t / 4) * 128>(kaddr[t % 4]);
+                x[1] = k_read<(t / 4) * 128 + 32 * DQK * 2>(kaddr[t % 4]);
+            };
+            auto mm = [&](i32x4_t(&x)[2], auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]), qf[t], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[1]), qf[t], sacc[1], 0, 0, 0);
+            };
+            rd(f[0], std::integral_constant<int, 0>{});
+            [&]<int... T>(std::integer_sequence<int, T...>) {
+                (([&] {
+                    constexpr int t = T;
+                    if constexpr (t + 1 < DQK / 16) {
+                        rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
+                        k_wait<2>(f[t & 1][0], f[t & 1][1]);
+                    } else {
+                        k_wait<0>(f[t & 1][0], f[t & 1][1]);
+                    }
+                    mm(f[t & 1], std::integral_constant<int, t>{});
+                }()),
+                 ...);
+            }(std::make_integer_sequence<int, DQK / 16>{});
+        }
+        // Accumulator element j of this lane holds key
+        //   kt + 32*kb + 8*(j/4) + 4*half + (j%4)   for query column `col`.
+        if (kt >= full_end) {
+            const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+        mx = fmaxf(mx, other_half(mx));
+        // Move the reference max only when it grew by more than the threshold
+        // for some row of the wave (first tile; rare afterwards).
+        const float m_cand = fmaxf(m_i, mx);
+        const bool grow = (m_cand - m_i) * cl2 > kRescaleThreshold;  // false while nothing is visible
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_cand : m_i;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m_i - m_new) * cl2) : 1.0f;
+            l_i *= alpha;
+#pragma unroll
+            for (int c = 0; c < DV / 32; ++c)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
+            m_i = m_new;
+        }
+        const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                pf[kb][j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
+        // Row sum of the rounded weights, so O is their exact weighted mean.
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2)
+                    l_i = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, l_i, false);
+
+        // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
+        // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
+        // the two transpose reads give this lane's value column at keys
+        // 32kb + 16u + 4half + 0..3 and + 8..11.  Step n + 1's reads are
+        // issued before step n's MFMAs.
+        static_assert(DV == 128 || DV == 64, "GEMM1 read schedule covers D_v of 64 and 128");
+        uint32_t vaddr[DV / 32];
+#pragma unroll
+        for (int c = 0; c < DV / 32; ++c) vaddr[c] = lds_addr(Vb + v_key * DV + (((4 * c + v_q) ^ v_sw) * 8) + v_in);
+        s16x4 xa[8], xb[8];
+        auto issue_step = [&](s16x4(&x)[8], auto kb_c, auto u_c) {
+            constexpr int kb = decltype(kb_c)::value, u = decltype(u_c)::value;
+            constexpr int o0 = (kb * 32 + u * 16) * DV * 2, o1 = o0 + 8 * DV * 2;
+#pragma unroll
+            for (int c = 0; c < DV / 32; ++c) {
+                x[2 * c] = tr_read<o0>(vaddr[c]);
+                x[2 * c + 1] = tr_read<o1>(vaddr[c]);
+            }
+#pragma unroll
+            for (int c = DV / 32; c < 4; ++c) x[2 * c] = x[2 * c + 1] = s16x4{0, 0, 0, 0};
+        };
+        auto mma_step = [&](s16x4(&x)[8], const bf16x8& p) {
+#pragma unroll
+            for (int c = 0; c < DV / 32; ++c) {
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * c], x[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+                o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[c], 0, 0, 0);
+            }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        constexpr int kReads = DV / 16;  // reads per step
+        issue_step(xa, I0{}, I0{});
+        issue_step(xb, I0{}, I1{});
+        tr_wait<kReads>(xa);
+        mma_step(xa, pf[0][0]);
+        issue_step(xa, I1{}, I0{});
+        tr_wait<kReads>(xb);
+        mma_step(xb, pf[0][1]);
+        issue_step(xb, I1{}, I1{});
+        tr_wait<kReads>(xa);
+        mma_step(xa, pf[1][0]);
+        tr_wait<0>(xb);
+        mma_step(xb, pf[1][1]);
+    };
+
     if (ks < ke) issue(ks, smem);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     int cur = 0;
     for (int kt = ks; kt < ke; kt += kBN) {
-        uint16_t* Kb = smem + cur * C::BUF_ELEMS;
-        uint16_t* Vb = Kb + C::K_ELEMS;
+        const uint16_t* Kb = smem + cur * C::BUF_ELEMS;
+        const uint16_t* Vb = Kb + C::K_ELEMS;
         if (kt + kBN < ke) issue(kt + kBN, smem + (cur ^ 1) * C::BUF_ELEMS);
-
         if (wave_active) {
-            // GEMM0: S^T[key][query] for two 32-key blocks.
-            f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-#pragma unroll
-            for (int t = 0; t < DQK / 16; ++t) {
-                const int pos = ((2 * t + half) ^ k_x) * 8;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * DQK + k_rd + pos);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
-                }
-            }
-            // Accumulator element j of this lane holds key
-            //   kt + 32*kb + 8*(j/4) + 4*half + (j%4)   for query column `col`.
-            const bool full = (kt + kBN <= ke) && ((int64_t)kt + kBN - 1 <= vis_first);
-            if (!full) {
-                const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // Move the reference max only when it grew by more than the
-            // threshold for some row of the wave (rare after the first tiles).
-            const float m_cand = fmaxf(m_i, mx);
-            const bool grow = (m_cand - m_i) * cl2 > kRescaleThreshold;  // false while nothing is visible
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? m_cand : m_i;
-                const float alpha = grow ? __builtin_amdgcn_exp2f((m_i - m_new) * cl2) : 1.0f;
-                l_i *= alpha;
-#pragma unroll
-                for (int c = 0; c < DV / 32; ++c)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
-                m_i = m_new;
-            }
-            const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
-
-            // P (rounded to bf16) in the B-operand layout of GEMM1; the row
-            // sum adds the rounded weights, so O is their exact weighted mean.
-            bf16x8 pf[2][2];
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; j += 2) {
-                    bf16x2 p2;
-                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
-                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], cl2, -mc));
-                    pf[kb][j >> 3][j & 7] = p2[0];
-                    pf[kb][j >> 3][(j & 7) + 1] = p2[1];
-                    l_i = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_i, false);
-                }
-
-            // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
-            // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
-            // the two transpose reads give this lane's value column at keys
-            // 32kb + 16u + 4half + 0..3 and + 8..11.  Step n + 1's reads are
-            // issued before step n's MFMAs.
-            static_assert(DV == 128 || DV == 64, "GEMM1 read schedule covers D_v of 64 and 128");
-            uint32_t vaddr[DV / 32];
-#pragma unroll
-            for (int c = 0; c < DV / 32; ++c) vaddr[c] = lds_addr(Vb + v_key * DV + (((4 * c + v_q) ^ v_sw) * 8) + v_in);
-            s16x4 xa[8], xb[8];
-            auto issue_step = [&](s16x4(&x)[8], auto kb_c, auto u_c) {
-                constexpr int kb = decltype(kb_c)::value, u = decltype(u_c)::value;
-                constexpr int o0 = (kb * 32 + u * 16) * DV * 2, o1 = o0 + 8 * DV * 2;
-#pragma unroll
-                for (int c = 0; c < DV / 32; ++c) {
-                    x[2 * c] = tr_read<o0>(vaddr[c]);
-                    x[2 * c + 1] = tr_read<o1>(vaddr[c]);
-                }
-#pragma unroll
-                for (int c = DV / 32; c < 4; ++c) x[2 * c] = x[2 * c + 1] = s16x4{0, 0, 0, 0};
-            };
-            auto mma_step = [&](s16x4(&x)[8], const bf16x8& p) {
-#pragma unroll
-                for (int c = 0; c < DV / 32; ++c) {
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * c], x[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[c], 0, 0, 0);
-                }
-            };
-            using I0 = std::integral_constant<int, 0>;
-            using I1 = std::integral_constant<int, 1>;
-            constexpr int kReads = DV / 16;  // reads per step
-            issue_step(xa, I0{}, I0{});
-            issue_step(xb, I0{}, I1{});
-            tr_wait<kReads>(xa);
-            mma_step(xa, pf[0][0]);
-            issue_step(xa, I1{}, I0{});
-            tr_wait<kReads>(xb);
-            mma_step(xb, pf[0][1]);
-            issue_step(xb, I1{}, I1{});
-            tr_wait<kReads>(xa);
-            mma_step(xa, pf[1][0]);
-            tr_wait<0>(xb);
-            mma_step(xb, pf[1][1]);
+            tile(kt, Kb, Vb);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of the next tile landed
         __syncthreads();                     // all loads landed, every wave is done with `cur`
@@ -343,7 +400,7 @@ void partial_bf16_kernel(PartialArgs a) {
     if (!row_ok) return;
     const int64_t prow = sq.row0 + qrow;
     if (prow >= a.rows) return;
-    const float l_tot = l_i + __shfl_xor(l_i, 32);
+    const float l_tot = l_i + other_half(l_i);
     const bool empty = (m_i == -INFINITY);  // no visible key in this split
     const float inv = empty ? 0.f : 1.0f / l_tot;
     const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
