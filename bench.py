@@ -144,11 +144,13 @@ def main() -> int:
     t_partial = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     t_combine = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
-    # combine after evicting L2 and the 256 MB infinity cache
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    # combine after evicting L2 and the 256 MB infinity cache: reading a
+    # 512 MB buffer leaves no dirty lines whose write-back would be charged
+    # to the combine
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_iters):
-        flush.zero_()
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
