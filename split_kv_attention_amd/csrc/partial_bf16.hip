@@ -69,8 +69,14 @@ __device__ __forceinline__ int k_swz(int r, int c) { return c ^ (r & 7); }
 template <int VG>
 __device__ __forceinline__ int v_swz(int r, int q) { return q ^ (4 * (r % VG)); }
 
-__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+// Buffer resource over [base, base + bytes): loads past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds_wave_base + 16 * lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint16_t* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voffset, 0, 0, 0);
 }
 
 // LDS byte address of a pointer into shared memory.
@@ -197,36 +203,34 @@ void partial_bf16_kernel(PartialArgs a) {
     float l_i = 0.f;        // sum of weights over this half-wave's keys
     const float cl2 = a.scale_log2;
 
-    // Direct HBM -> LDS tile loads.  Load i of this thread fills LDS chunk
-    // P = 256 i + tid of the tile (a wave covers 64 consecutive chunks); the
-    // chunk holds row P / CH and, after the swizzle, column chunk c of that row.
-    const int k_row32 = (int)a.k_row, v_row32 = (int)a.v_row;
-    int k_r[C::K_LOADS], k_c[C::K_LOADS], v_r[C::V_LOADS], v_c[C::V_LOADS];
+    // Direct HBM -> LDS tile loads (buffer_load ... lds).  Load i of this
+    // thread fills LDS chunk P = 256 i + tid of the tile (a wave covers 64
+    // consecutive chunks); the chunk holds row P / CH and, after the swizzle,
+    // column chunk c of that row.  The byte offset from the tile's first key
+    // is the same for every tile.
+    uint32_t k_off[C::K_LOADS], v_off[C::V_LOADS];
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i) {
         const int P = i * kThreads + tid;
-        k_r[i] = P / C::KCH;
-        k_c[i] = k_swz(k_r[i], P % C::KCH) * 8;
+        const int r = P / C::KCH;
+        k_off[i] = (uint32_t)(r * a.k_row + k_swz(r, P % C::KCH) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
         const int P = i * kThreads + tid;
-        v_r[i] = P / C::VCH;
-        v_c[i] = v_swz<C::VG>(v_r[i], P % C::VCH) * 8;
+        const int r = P / C::VCH;
+        v_off[i] = (uint32_t)(r * a.v_row + v_swz<C::VG>(r, P % C::VCH) * 8) * 2u;
     }
-    // Rows past the split's end load the split's last key instead (valid
-    // memory, finite values): their scores are masked to -inf, weights 0.
+    // The buffer range of a tile ends with the split's last key, so rows past
+    // it read as zeros (finite): their scores are masked to -inf, weights 0.
     auto issue = [&](int kt, uint16_t* buf) {
-        const uint16_t* kt_ptr = kbase + (int64_t)kt * a.k_row;
-        const uint16_t* vt_ptr = vbase + (int64_t)kt * a.v_row;
-        const int last = min(ke - 1 - kt, kBN - 1);
+        const int rows = min(ke - kt, kBN);
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + (int64_t)kt * a.k_row, (uint32_t)(((rows - 1) * a.k_row + DQK) * 2));
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + (int64_t)kt * a.v_row, (uint32_t)(((rows - 1) * a.v_row + DV) * 2));
 #pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i)
-            load_lds16(kt_ptr + min(k_r[i], last) * k_row32 + k_c[i], buf + (i * kThreads + wave * 64) * 8);
+        for (int i = 0; i < C::K_LOADS; ++i) load_lds16(kr, k_off[i], buf + (i * kThreads + wave * 64) * 8);
 #pragma unroll
-        for (int i = 0; i < C::V_LOADS; ++i)
-            load_lds16(vt_ptr + min(v_r[i], last) * v_row32 + v_c[i],
-                       buf + C::K_ELEMS + (i * kThreads + wave * 64) * 8);
+        for (int i = 0; i < C::V_LOADS; ++i) load_lds16(vr, v_off[i], buf + C::K_ELEMS + (i * kThreads + wave * 64) * 8);
     };
 
     // Per-lane LDS read offsets (elements).  GEMM0: K row kb*32 + col, chunk

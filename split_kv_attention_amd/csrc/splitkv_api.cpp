@@ -181,6 +181,9 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
         if (s % vec) return fail(SK_ERR_UNSUPPORTED, "Q/K/V strides must be multiples of %d elements", vec);
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
         return fail(SK_ERR_UNSUPPORTED, "Q/K/V/o_part must be 16-byte aligned");
+    // Key tiles are addressed with 32-bit byte offsets from the tile's first key.
+    if (p->k_stride_row > ((int64_t)1 << 24) || p->v_stride_row > ((int64_t)1 << 24))
+        return fail(SK_ERR_UNSUPPORTED, "K/V row strides above 2^24 elements are not supported");
 
     const int64_t n_tiles = (p->max_seqlen_q + kern.m_per_block - 1) / kern.m_per_block;
     const int64_t n_work = n_tiles * p->num_heads * p->split_kv * (int64_t)p->batch;
