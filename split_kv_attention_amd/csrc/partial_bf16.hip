@@ -63,9 +63,18 @@ struct Cfg {
 };
 
 // LDS position (in 16-byte chunks within the row) of chunk c of K row r, and
-// of chunk q of V row r.  K: GEMM0 reads one chunk of 32 consecutive rows;
-// V: the transpose reads take 64 bytes of 4 consecutive rows.
-__device__ __forceinline__ int k_swz(int r, int c) { return c ^ (r & 7); }
+// of chunk q of V row r.  gfx950 serves 16 lanes of a 128-bit read per
+// cycle from 64 banks (256 bytes), so the 16 rows GEMM0 reads together must
+// fall into 16 different 16-byte bank groups.  With KCH = 8 (mod 16) rows
+// start alternately at group 0 and 8, and c ^ ((r >> 1) & 7) spreads each
+// pair over the other 8 groups; with KCH = 0 (mod 16), c ^ (r & 15).  V: the
+// transpose reads take 64 bytes of 4 consecutive rows; 4 (r % 4) moves each
+// of those rows to its own quarter of the banks.
+template <int KCH>
+__device__ __forceinline__ int k_swz(int r, int c) {
+    if constexpr (KCH % 16 == 0) return c ^ (r & 15);
+    else return c ^ ((r >> 1) & 7);
+}
 template <int VG>
 __device__ __forceinline__ int v_swz(int r, int q) { return q ^ (4 * (r % VG)); }
 
@@ -164,7 +173,7 @@ void partial_bf16_kernel(PartialArgs a) {
     const int64_t vis_first = vis_last(sq, mask, r0);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases in SGPRs
     const int lane = tid & 63;
     const int col = lane & 31;   // query column of this lane (and A-row for loads)
     const int half = lane >> 5;  // which 8-wide k slice / which 4 accumulator rows
@@ -213,7 +222,7 @@ void partial_bf16_kernel(PartialArgs a) {
     for (int i = 0; i < C::K_LOADS; ++i) {
         const int P = i * kThreads + tid;
         const int r = P / C::KCH;
-        k_off[i] = (uint32_t)(r * a.k_row + k_swz(r, P % C::KCH) * 8) * 2u;
+        k_off[i] = (uint32_t)(r * a.k_row + k_swz<C::KCH>(r, P % C::KCH) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
@@ -221,16 +230,33 @@ void partial_bf16_kernel(PartialArgs a) {
         const int r = P / C::VCH;
         v_off[i] = (uint32_t)(r * a.v_row + v_swz<C::VG>(r, P % C::VCH) * 8) * 2u;
     }
+    // LDS: K tiles in two slots, V tiles in two slots.  K runs one tile ahead
+    // of V: while tile t is in its softmax and GEMM1, GEMM0 of tile t + 1
+    // reads the other K slot.
+    uint16_t* const Ks0 = smem;
+    uint16_t* const Vs0 = smem + 2 * C::K_ELEMS;
     // The buffer range of a tile ends with the split's last key, so rows past
     // it read as zeros (finite): their scores are masked to -inf, weights 0.
-    auto issue = [&](int kt, uint16_t* buf) {
+    // A tile starting at or past the end has an empty range and loads zeros.
+    auto tile_bytes = [&](int kt, int64_t row, int d) -> uint32_t {
         const int rows = min(ke - kt, kBN);
-        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + (int64_t)kt * a.k_row, (uint32_t)(((rows - 1) * a.k_row + DQK) * 2));
-        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + (int64_t)kt * a.v_row, (uint32_t)(((rows - 1) * a.v_row + DV) * 2));
+        return rows > 0 ? (uint32_t)(((rows - 1) * row + d) * 2) : 0u;
+    };
+    auto issue_k = [&](int kt, int slot) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase + (int64_t)kt * a.k_row, tile_bytes(kt, a.k_row, DQK));
+        uint16_t* dst = Ks0 + slot * C::K_ELEMS;
 #pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i) load_lds16(kr, k_off[i], buf + (i * kThreads + wave * 64) * 8);
+        for (int i = 0; i < C::K_LOADS; ++i) load_lds16(r, k_off[i], dst + (i * kThreads + wave * 64) * 8);
+    };
+    auto issue_v = [&](int kt, int slot) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase + (int64_t)kt * a.v_row, tile_bytes(kt, a.v_row, DV));
+        uint16_t* dst = Vs0 + slot * C::V_ELEMS;
 #pragma unroll
-        for (int i = 0; i < C::V_LOADS; ++i) load_lds16(vr, v_off[i], buf + C::K_ELEMS + (i * kThreads + wave * 64) * 8);
+        for (int i = 0; i < C::V_LOADS; ++i) load_lds16(r, v_off[i], dst + (i * kThreads + wave * 64) * 8);
+    };
+    auto sync_tiles = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads landed
+        __syncthreads();                     // everyone's landed; every wave is done with the old slots
     };
 
     // Per-lane LDS read offsets (elements).  GEMM0: K row kb*32 + col, chunk
@@ -238,7 +264,6 @@ void partial_bf16_kernel(PartialArgs a) {
     // 16-lane group addresses key (4h + s/4 [+8]) and value columns
     // 32c + 16 g2 + 4 (s%4) .. +3, g2 = (lane / 16) % 2.
     const int k_rd = col * DQK;
-    const int k_x = col & 7;
     const int s16 = lane & 15;
     const int g2 = (lane >> 4) & 1;
     const int v_key = half * 4 + (s16 >> 2);
@@ -250,50 +275,54 @@ void partial_bf16_kernel(PartialArgs a) {
     const int64_t full_last = min((int64_t)ke - kBN, vis_first - (kBN - 1));  // last unmasked tile start
     const int full_end = full_last < ks ? ks : (int)(ks + ((full_last - ks) / kBN + 1) * kBN);
 
-    // One key tile: GEMM0, softmax, GEMM1.  Tiles from full_end on (the
-    // ragged end of the split, or keys beyond some row's causal limit) are
-    // masked per element.
-    auto tile = [&](int kt, const uint16_t* Kb, const uint16_t* Vb) {
-        // GEMM0: S^T[key][query] for two 32-key blocks; K fragments for step
-        // t + 1 are read while step t multiplies.
-        f32x16 sacc[2];
+    // GEMM0: S^T[key][query] for the two 32-key blocks of tile Kb; K
+    // fragments for step t + 1 are read while step t multiplies.
+    auto gemm0 = [&](const uint16_t* Kb, f32x16(&sacc)[2], auto&& side) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-        {
-            // per-lane bases: chunk (2(t%4) + half) ^ (col & 7); t/4 adds 128 bytes
-            uint32_t kaddr[4];
+        // per-lane bases: chunk (2t + half) ^ f(row) with f < 16 (or < 8)
+        // changes only the low 4 (3) bits, so t / 8 (t / 4) steps add whole
+        // 256-byte (128-byte) blocks
+        constexpr int kSpan = (C::KCH % 16 == 0) ? 8 : 4;  // steps per repeating block
+        uint32_t kaddr[kSpan];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) kaddr[m] = lds_addr(Kb + k_rd + (((2 * m + half) ^ k_x) * 8));
-            i32x4_t f[2][2];
-            auto rd = [&](i32x4_t(&x)[2], auto t_c) {
-                constexpr int t = decltype(t_c)::value;
-                x[0] = k_read<(t / 4) * 128>(kaddr[t % 4]);
-                x[1] = k_read<(t / 4) * 128 + 32 * DQK * 2>(kaddr[t % 4]);
-            };
-            auto mm = [&](i32x4_t(&x)[2], auto t_c) {
-                constexpr int t = decltype(t_c)::value;
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]), qf[t], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[1]), qf[t], sacc[1], 0, 0, 0);
-            };
-            rd(f[0], std::integral_constant<int, 0>{});
-            [&]<int... T>(std::integer_sequence<int, T...>) {
-                (([&] {
-                    constexpr int t = T;
-                    if constexpr (t + 1 < DQK / 16) {
-                        rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
-                        k_wait<2>(f[t & 1][0], f[t & 1][1]);
-                    } else {
-                        k_wait<0>(f[t & 1][0], f[t & 1][1]);
-                    }
-                    mm(f[t & 1], std::integral_constant<int, t>{});
-                }()),
-                 ...);
-            }(std::make_integer_sequence<int, DQK / 16>{});
-        }
-        // Accumulator element j of this lane holds key
-        //   kt + 32*kb + 8*(j/4) + 4*half + (j%4)   for query column `col`.
+        for (int m = 0; m < kSpan; ++m) kaddr[m] = lds_addr(Kb + k_rd + (k_swz<C::KCH>(col, 2 * m + half) * 8));
+        i32x4_t f[2][2];
+        auto rd = [&](i32x4_t(&x)[2], auto t_c) {
+            constexpr int t = decltype(t_c)::value;
+            x[0] = k_read<(t / kSpan) * kSpan * 32>(kaddr[t % kSpan]);
+            x[1] = k_read<(t / kSpan) * kSpan * 32 + 32 * DQK * 2>(kaddr[t % kSpan]);
+        };
+        auto mm = [&](i32x4_t(&x)[2], auto t_c) {
+            constexpr int t = decltype(t_c)::value;
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]), qf[t], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[1]), qf[t], sacc[1], 0, 0, 0);
+        };
+        rd(f[0], std::integral_constant<int, 0>{});
+        [&]<int... T>(std::integer_sequence<int, T...>) {
+            (([&] {
+                constexpr int t = T;
+                if constexpr (t + 1 < DQK / 16) {
+                    rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
+                    k_wait<2>(f[t & 1][0], f[t & 1][1]);
+                } else {
+                    k_wait<0>(f[t & 1][0], f[t & 1][1]);
+                }
+                mm(f[t & 1], std::integral_constant<int, t>{});
+                side(std::integral_constant<int, t>{});
+            }()),
+             ...);
+        }(std::make_integer_sequence<int, DQK / 16>{});
+    };
+    auto no_side = [](auto) {};
+
+    // Masking (tiles from full_end on) and the reference-max update of a
+    // tile whose scores are complete.  Accumulator element j of a lane holds
+    // key kt + 32*kb + 8*(j/4) + 4*half + (j%4) for query column `col`.
+    auto mask_and_max = [&](int kt, f32x16(&sacc)[2]) {
         if (kt >= full_end) {
+            asm volatile("");  // a real branch: most tiles need no mask
             const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -301,7 +330,6 @@ void partial_bf16_kernel(PartialArgs a) {
                 for (int j = 0; j < 16; ++j)
                     if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
         }
-
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -309,7 +337,8 @@ void partial_bf16_kernel(PartialArgs a) {
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
         mx = fmaxf(mx, other_half(mx));
         // Move the reference max only when it grew by more than the threshold
-        // for some row of the wave (first tile; rare afterwards).
+        // for some row of the wave (first tile; rare afterwards).  The output
+        // accumulated so far is rescaled before this tile is added.
         const float m_cand = fmaxf(m_i, mx);
         const bool grow = (m_cand - m_i) * cl2 > kRescaleThreshold;  // false while nothing is visible
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -322,14 +351,18 @@ void partial_bf16_kernel(PartialArgs a) {
                 for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
             m_i = m_new;
         }
+    };
+
+    // Weights of a tile (rounded to bf16, in GEMM1's B-operand layout) and
+    // their row sum, which adds the rounded values so O is their exact
+    // weighted mean.
+    auto weights = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2]) {
         const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
-        bf16x8 pf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 pf[kb][j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
-        // Row sum of the rounded weights, so O is their exact weighted mean.
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -339,12 +372,43 @@ void partial_bf16_kernel(PartialArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; j += 2)
                     l_i = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, l_i, false);
-
-        // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
-        // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
-        // the two transpose reads give this lane's value column at keys
-        // 32kb + 16u + 4half + 0..3 and + 8..11.  Step n + 1's reads are
-        // issued before step n's MFMAs.
+    };
+    // The same, a slice of 2E elements at a time (E pairs), to be spread
+    // over the steps of the next tile's GEMM0.
+    constexpr int kSteps = DQK / 16;
+    constexpr int kPairsPerStep = (16 + kSteps - 1) / kSteps;
+    auto weights_slice = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float mc_in, auto step_c) {
+        constexpr int step = decltype(step_c)::value;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        if constexpr (step * kPairsPerStep < 16) {
+            float mc = mc_in;
+            asm volatile("" : "+v"(mc));  // keeps this slice below the step's wait
+#pragma unroll
+            for (int q = 0; q < kPairsPerStep; ++q) {
+                const int pr = step * kPairsPerStep + q;  // pair index 0..15
+                if (pr < 16) {
+                    const int e = 2 * pr;  // element 0..31 = 16 kb + j
+                    const int kb = e >> 4, j = e & 15;
+                    bf16x2 p2;
+                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
+                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], cl2, -mc));
+                    uint32_t packed = __builtin_bit_cast(uint32_t, p2);
+                    asm volatile("" : "+v"(packed));  // keeps it above the next step's reads
+                    p2 = __builtin_bit_cast(bf16x2, packed);
+                    pf[kb][j >> 3][j & 7] = p2[0];
+                    pf[kb][j >> 3][(j & 7) + 1] = p2[1];
+                    l_i = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_i, false);
+                }
+            }
+        }
+    };
+    // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
+    // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
+    // the two transpose reads give this lane's value column at keys
+    // 32kb + 16u + 4half + 0..3 and + 8..11.  Step n + 1's reads are issued
+    // before step n's MFMAs.
+    auto gemm1 = [&](const uint16_t* Vb, const bf16x8(&pf)[2][2]) {
         static_assert(DV == 128 || DV == 64, "GEMM1 read schedule covers D_v of 64 and 128");
         uint32_t vaddr[DV / 32];
 #pragma unroll
@@ -385,20 +449,42 @@ void partial_bf16_kernel(PartialArgs a) {
         mma_step(xb, pf[1][1]);
     };
 
-    if (ks < ke) issue(ks, smem);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    int cur = 0;
-    for (int kt = ks; kt < ke; kt += kBN) {
-        const uint16_t* Kb = smem + cur * C::BUF_ELEMS;
-        const uint16_t* Vb = Kb + C::K_ELEMS;
-        if (kt + kBN < ke) issue(kt + kBN, smem + (cur ^ 1) * C::BUF_ELEMS);
+    // Pipeline.  Iteration i: DMA K(i+2) -> K slot i%2 and V(i+1) -> V slot
+    // (i+1)%2; GEMM0(i+1) from K slot (i+1)%2 together with the weights of
+    // tile i; GEMM1(i) from V slot i%2; then tile i+1's mask / max update.
+    const int ntiles = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
+    if (ntiles > 0) {
+        issue_k(ks, 0);
+        issue_v(ks, 0);
+        sync_tiles();
+        issue_k(ks + kBN, 1);
+        f32x16 sc[2];
         if (wave_active) {
-            tile(kt, Kb, Vb);
+            gemm0(Ks0, sc, no_side);
+            mask_and_max(ks, sc);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of the next tile landed
-        __syncthreads();                     // all loads landed, every wave is done with `cur`
-        cur ^= 1;
+        sync_tiles();
+        for (int i = 0; i + 1 < ntiles; ++i) {
+            const int kt = ks + i * kBN;
+            issue_k(kt + 2 * kBN, i & 1);
+            issue_v(kt + kBN, (i + 1) & 1);
+            if (wave_active) {
+                f32x16 sn[2];
+                bf16x8 pf[2][2];
+                const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
+                gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sn, [&](auto step_c) { weights_slice(sc, pf, mc, step_c); });
+                gemm1(Vs0 + (i & 1) * C::V_ELEMS, pf);
+                mask_and_max(kt + kBN, sn);
+                sc[0] = sn[0];
+                sc[1] = sn[1];
+            }
+            sync_tiles();
+        }
+        if (wave_active) {
+            bf16x8 pf[2][2];
+            weights(sc, pf);
+            gemm1(Vs0 + ((ntiles - 1) & 1) * C::V_ELEMS, pf);
+        }
     }
 
     if (!row_ok) return;
