@@ -317,28 +317,27 @@ void partial_bf16_kernel(PartialArgs a) {
     };
     auto no_side = [](auto) {};
 
-    // Masking (tiles from full_end on) and the reference-max update of a
-    // tile whose scores are complete.  Accumulator element j of a lane holds
-    // key kt + 32*kb + 8*(j/4) + 4*half + (j%4) for query column `col`.
-    auto mask_and_max = [&](int kt, f32x16(&sacc)[2]) {
-        if (kt >= full_end) {
-            asm volatile("");  // a real branch: most tiles need no mask
-            const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
+    // Masking of a tile from full_end on.  Accumulator element j of a lane
+    // holds key kt + 32*kb + 8*(j/4) + 4*half + (j%4) for query column `col`.
+    auto mask_tile = [&](int kt, f32x16(&sacc)[2]) {
+        const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
-        }
+            for (int j = 0; j < 16; ++j)
+                if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
+    };
+    // Reference-max update from a tile's complete scores.  The reference max
+    // moves only when it grew by more than the threshold for some row of the
+    // wave; the output accumulated so far is rescaled before this tile's
+    // weights are added.
+    auto max_update = [&](const f32x16(&sacc)[2]) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
         mx = fmaxf(mx, other_half(mx));
-        // Move the reference max only when it grew by more than the threshold
-        // for some row of the wave (first tile; rare afterwards).  The output
-        // accumulated so far is rescaled before this tile is added.
         const float m_cand = fmaxf(m_i, mx);
         const bool grow = (m_cand - m_i) * cl2 > kRescaleThreshold;  // false while nothing is visible
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -352,11 +351,31 @@ void partial_bf16_kernel(PartialArgs a) {
             m_i = m_new;
         }
     };
+    // First tile and masked tiles take the reference-max update before their
+    // weights.  Later unmasked tiles skip it: every row already has a finite
+    // reference (the first tile was unmasked), their weights are computed
+    // against it, and only if some row's weight sum leaves [0, 2^64] (a score
+    // more than 64 / (scale log2 e) above the reference, or inf) the update
+    // is taken and the weights recomputed.  Below that bound weights, sums
+    // and the output accumulator stay far inside f32 / bf16 range, and the
+    // result O = sum p V / sum p does not depend on the reference.
+    auto prepare = [&](int kt, f32x16(&sacc)[2]) -> bool {
+        const bool masked = kt >= full_end;
+        if (masked) {
+            asm volatile("");  // a real branch: most tiles need no mask
+            mask_tile(kt, sacc);
+        }
+        if (masked || kt == ks) {
+            max_update(sacc);
+            return true;
+        }
+        return false;
+    };
 
     // Weights of a tile (rounded to bf16, in GEMM1's B-operand layout) and
-    // their row sum, which adds the rounded values so O is their exact
+    // their row sum rs, which adds the rounded values so O is their exact
     // weighted mean.
-    auto weights = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2]) {
+    auto weights = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float& rs) {
         const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -365,19 +384,20 @@ void partial_bf16_kernel(PartialArgs a) {
                 pf[kb][j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int j = 0; j < 8; j += 2)
-                    l_i = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, l_i, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, rs, false);
     };
     // The same, a slice of 2E elements at a time (E pairs), to be spread
     // over the steps of the next tile's GEMM0.
     constexpr int kSteps = DQK / 16;
     constexpr int kPairsPerStep = (16 + kSteps - 1) / kSteps;
-    auto weights_slice = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float mc_in, auto step_c) {
+    auto weights_slice = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float mc_in, float& rs, auto step_c) {
         constexpr int step = decltype(step_c)::value;
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -398,10 +418,18 @@ void partial_bf16_kernel(PartialArgs a) {
                     p2 = __builtin_bit_cast(bf16x2, packed);
                     pf[kb][j >> 3][j & 7] = p2[0];
                     pf[kb][j >> 3][(j & 7) + 1] = p2[1];
-                    l_i = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_i, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, rs, false);
                 }
             }
         }
+    };
+    // Range check of weights computed without the max update (see prepare).
+    auto check_weights = [&](bool max_taken, const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float& rs) {
+        if (!max_taken && __builtin_amdgcn_ballot_w64(!(rs <= 0x1p64f))) {
+            max_update(sacc);
+            weights(sacc, pf, rs);
+        }
+        l_i += rs;
     };
     // GEMM1: O^T[value][query] += V^T[value][key] P^T[key][query].
     // B element j' of step (kb, u) is key 32kb + 16u + 8(j'/4) + 4half + j'%4;
@@ -459,9 +487,10 @@ void partial_bf16_kernel(PartialArgs a) {
         sync_tiles();
         issue_k(ks + kBN, 1);
         f32x16 sc[2];
+        bool sc_max = true;  // whether tile sc took the reference-max update
         if (wave_active) {
             gemm0(Ks0, sc, no_side);
-            mask_and_max(ks, sc);
+            sc_max = prepare(ks, sc);
         }
         sync_tiles();
         for (int i = 0; i + 1 < ntiles; ++i) {
@@ -471,10 +500,12 @@ void partial_bf16_kernel(PartialArgs a) {
             if (wave_active) {
                 f32x16 sn[2];
                 bf16x8 pf[2][2];
+                float rs = 0.f;
                 const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
-                gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sn, [&](auto step_c) { weights_slice(sc, pf, mc, step_c); });
+                gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sn, [&](auto step_c) { weights_slice(sc, pf, mc, rs, step_c); });
+                check_weights(sc_max, sc, pf, rs);
                 gemm1(Vs0 + (i & 1) * C::V_ELEMS, pf);
-                mask_and_max(kt + kBN, sn);
+                sc_max = prepare(kt + kBN, sn);
                 sc[0] = sn[0];
                 sc[1] = sn[1];
             }
@@ -482,7 +513,9 @@ void partial_bf16_kernel(PartialArgs a) {
         }
         if (wave_active) {
             bf16x8 pf[2][2];
-            weights(sc, pf);
+            float rs;
+            weights(sc, pf, rs);
+            check_weights(sc_max, sc, pf, rs);
             gemm1(Vs0 + ((ntiles - 1) & 1) * C::V_ELEMS, pf);
         }
     }

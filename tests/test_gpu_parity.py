@@ -240,3 +240,20 @@ def test_full_prefill_sampled_rows(w):
     assert torch.isfinite(res["out"]).all()
     del inputs, res
     torch.cuda.empty_cache()
+
+
+def test_scores_growing_far_beyond_the_first_tile():
+    """Keys after the first tile with ~50x larger scores: unmasked tiles that
+    skip the running-max update must fall back to it (their weights would
+    overflow), and the result still matches the oracle."""
+    for mask in ("none", "causal"):
+        w = _shrink(workloads.CAUSAL_BF16, name=f"growth_{mask}", mask=mask, sq=(300, 300), sk=(700, 700),
+                    split_kv=2, heads=2)
+        inputs = workloads.make_inputs(w, DEV, 9)
+        k = inputs["k"].float()
+        k[:, :, 200:] *= 40.0
+        inputs["k"] = k.to(torch.bfloat16)
+        log(f"e2e {w.name}")
+        _, prob, res = run_gpu(w, inputs=inputs)
+        st = compare(w, inputs, prob, res, label=w.name)
+        log(f"  {st}")
