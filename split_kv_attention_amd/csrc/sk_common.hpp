@@ -89,17 +89,6 @@ __device__ __forceinline__ int32_t valid_split_count(const Seq& s, int mask, int
     return (int32_t)ceil_div64(rl + 1, keys_per_split(rl, n_per_block, s.splits));
 }
 
-// Workgroups are dealt round-robin over the 8 XCDs of an MI355X.  Remap the
-// hardware block index so that each XCD receives one contiguous range of work
-// items: neighbouring items (the query tiles of one head and split, which read
-// the same keys and values) then share that XCD's L2.  A bijection on [0, n).
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
-    constexpr uint32_t kXcds = 8;
-    const uint32_t q = n / kXcds, r = n % kXcds;
-    const uint32_t x = bid % kXcds, i = bid / kXcds;
-    return x * q + min(x, r) + i;
-}
-
 // Arguments of every partial-attention kernel.
 struct PartialArgs {
     const void* q;
@@ -124,15 +113,61 @@ struct WorkItem {
     int tile, head, split, batch;
 };
 
+// Keys of split s of sequence `sq` under the partition of its last query
+// block (the block with the most keys under causal masking): used only to
+// order work, never to compute.
+__device__ __forceinline__ int64_t split_keys(const Seq& sq, int mask, int n_per_block, int s) {
+    if (sq.sq <= 0 || s >= sq.splits) return 0;
+    const int64_t rl = row_last(sq, mask, sq.sq - 1);
+    const int64_t kps = keys_per_split(rl, n_per_block, sq.splits);
+    const int64_t kend = min(rl + 1, sq.lv + 1);
+    return max((int64_t)0, min((int64_t)(s + 1) * kps, kend) - min((int64_t)s * kps, kend));
+}
+
+// Rank r (0 = most keys) of the (sequence, split) pairs -> pair index.  For
+// at most 64 pairs every wave ranks them all, one pair per lane (ties keep
+// index order); otherwise the order is the identity.
+__device__ __forceinline__ uint32_t pair_by_rank(const PartialArgs& a, uint32_t r) {
+    const int npairs = (int)(a.n_work / ((uint32_t)a.n_tiles * a.heads));
+    if (npairs <= 1 || npairs > 64) return r;
+    const int lane = threadIdx.x & 63;
+    int64_t cost = -1;
+    if (lane < npairs) {
+        const Seq sq = load_seq(a.seqs, lane / a.seqs.s_max);
+        cost = split_keys(sq, a.seqs.mask, a.seqs.n_per_block, lane % a.seqs.s_max);
+    }
+    const int cost32 = (int)min(cost, (int64_t)0x7fffffff);
+    int rank = 0;
+    for (int j = 0; j < npairs; ++j) {
+        const int cj = __builtin_amdgcn_readlane(cost32, j);
+        rank += (cj > cost32) || (cj == cost32 && j < lane);
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < npairs && rank == (int)r);
+    return hit ? (uint32_t)__builtin_ctzll(hit) : r;
+}
+
+// Work items are groups (pair, head) of n_tiles query tiles each; groups are
+// ordered longest pair first.  Workgroups are dealt round-robin over the 8
+// XCDs of an MI355X (XCD = blockIdx.x % 8), so block b is mapped to give XCD x
+// the groups x, x + 8, x + 16, ... in that order: every XCD gets an equal
+// share of long and short groups, runs its longest first, and the tiles of
+// one group (which read the same keys and values) share its L2.  Groups past
+// the last multiple of 8 are spread tile by tile.  A bijection on [0, n_work).
 __device__ __forceinline__ WorkItem decode_work(const PartialArgs& a) {
-    uint32_t w = xcd_remap(blockIdx.x, a.n_work);
+    constexpr uint32_t kXcds = 8;
+    const uint32_t T = a.n_tiles, G = a.n_work / T, b = blockIdx.x;
+    uint32_t u = b;
+    if (b < (G / kXcds) * kXcds * T) {
+        const uint32_t x = b % kXcds, i = b / kXcds;
+        u = ((i / T) * kXcds + x) * T + i % T;
+    }
     WorkItem it;
-    it.tile = w % a.n_tiles;
-    w /= a.n_tiles;
-    it.head = w % a.heads;
-    w /= a.heads;
-    it.split = w % a.seqs.s_max;
-    it.batch = w / a.seqs.s_max;
+    it.tile = u % T;
+    u /= T;
+    it.head = u % a.heads;
+    const uint32_t pair = pair_by_rank(a, u / a.heads);
+    it.split = pair % a.seqs.s_max;
+    it.batch = pair / a.seqs.s_max;
     return it;
 }
 

@@ -110,6 +110,13 @@ SMALL = [
     _shrink(workloads.VARLEN_BATCH_PREFIX, name="varlen_prefix_small", sq=(130, 1, 257, 64), sk=(500, 70, 1500, 3000),
             split_kv_per_seq=(2, 4, 6, 8), prefix_offset_per_seq=(370, 69, 1243, 2936),
             last_valid_per_seq=(499, 69, 1499, 2999)),
+    # 63 (sequence, split) pairs: ranked longest first; 189 groups, not a multiple of the 8 XCDs
+    _shrink(workloads.VARLEN_BATCH, name="varlen_63_pairs_ranked", heads=3, split_kv=7, split_kv_per_seq=None,
+            sq=(33, 1, 70, 5, 128, 129, 2, 64, 17), sk=(900, 64, 1200, 31, 700, 2500, 5, 333, 1024)),
+    # 77 pairs: beyond the ranked range, identity order
+    _shrink(workloads.VARLEN_BATCH, name="varlen_77_pairs_unranked", heads=2, split_kv=7,
+            split_kv_per_seq=(7, 1, 3, 7, 5, 2, 7, 6, 4, 7, 1),
+            sq=(33, 1, 70, 5, 128, 129, 2, 64, 17, 200, 9), sk=(900, 64, 1200, 31, 700, 2500, 5, 333, 1024, 222, 4000)),
     _shrink(workloads.DECODE_BF16, name="decode_small_B4_H4_Sk3000", sq=(1,) * 4, sk=(3000,) * 4, heads=4),
     _shrink(workloads.CAUSAL_BF16, name="causal_d64_Sq200", d_qk=64, d_v=64, sq=(200, 200), sk=(333, 333)),
     _shrink(workloads.CAUSAL_BF16, name="prefix_negative_fully_masked", mask="prefix_causal", prefix_offset=-70,
