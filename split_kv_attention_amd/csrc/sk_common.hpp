@@ -187,11 +187,15 @@ struct CombineArgs {
     int64_t rows;
     int32_t heads;
     int32_t dv;
+    int32_t batch;
+    int32_t row_blocks;  // blocks per head (set by the launcher)
 };
 
 // Launchers (one translation unit each).
 hipError_t launch_counts(const CountsArgs& a, int batch, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, int batch, int out_dtype, hipStream_t stream);
+hipError_t launch_combine(CombineArgs a, int out_dtype, hipStream_t stream);
+// Blocks per head of the combine grid (rows_per_block = 256 / (dv / 4)).
+int64_t combine_row_blocks(int64_t batch, int64_t max_sq, int dv, bool packed);
 
 typedef hipError_t (*PartialLauncher)(const PartialArgs& a, hipStream_t stream);
 struct PartialKernel {

@@ -227,11 +227,9 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
         if (s % 4) return fail(SK_ERR_UNSUPPORTED, "out strides must be multiples of 4 elements");
     if (!aligned(out, 4 * elem_bytes(p->out_dtype)) || !aligned(o_part, 16))
         return fail(SK_ERR_UNSUPPORTED, "out / o_part are not aligned for 4-element vectors");
-    {
-        const int64_t parts = p->head_dim_v / 4, rows_per_block = parts <= 256 ? 256 / parts : 1;
-        if ((p->max_seqlen_q + rows_per_block - 1) / rows_per_block * p->num_heads >= ((int64_t)1 << 31))
-            return fail(SK_ERR_UNSUPPORTED, "problem too large for the combine grid");
-    }
+    if (sk::combine_row_blocks(p->batch, p->max_seqlen_q, p->head_dim_v, p->cu_seqlens_q != nullptr) *
+            p->num_heads >= ((int64_t)1 << 31))
+        return fail(SK_ERR_UNSUPPORTED, "problem too large for the combine grid");
     sk::CombineArgs a;
     a.o_part = o_part;
     a.lse_part = lse_part;
@@ -245,7 +243,9 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
     a.rows = rows;
     a.heads = p->num_heads;
     a.dv = p->head_dim_v;
-    return hip_status(sk::launch_combine(a, p->batch, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
+    a.batch = p->batch;
+    a.row_blocks = 0;
+    return hip_status(sk::launch_combine(a, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
 }
 
 }  // extern "C"

@@ -117,6 +117,11 @@ SMALL = [
     _shrink(workloads.VARLEN_BATCH, name="varlen_77_pairs_unranked", heads=2, split_kv=7,
             split_kv_per_seq=(7, 1, 3, 7, 5, 2, 7, 6, 4, 7, 1),
             sq=(33, 1, 70, 5, 128, 129, 2, 64, 17, 200, 9), sk=(900, 64, 1200, 31, 700, 2500, 5, 333, 1024, 222, 4000)),
+    # dense rows flattened across sequences in the combine: one block spans
+    # several sequences with their own split counts, offsets and last keys
+    _shrink(workloads.DECODE_BF16, name="dense_B7_Sq3_per_seq_params", sq=(3,) * 7, sk=(700,) * 7, heads=3,
+            split_kv=6, split_kv_per_seq=(1, 2, 3, 6, 5, 4, 6), mask="prefix_causal",
+            prefix_offset_per_seq=(697, 0, 300, -2, 696, 150, 650), last_valid_per_seq=(699, 699, 500, 699, -1, 99, 680)),
     _shrink(workloads.DECODE_BF16, name="decode_small_B4_H4_Sk3000", sq=(1,) * 4, sk=(3000,) * 4, heads=4),
     _shrink(workloads.CAUSAL_BF16, name="causal_d64_Sq200", d_qk=64, d_v=64, sq=(200, 200), sk=(333, 333)),
     _shrink(workloads.CAUSAL_BF16, name="prefix_negative_fully_masked", mask="prefix_causal", prefix_offset=-70,
