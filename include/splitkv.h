@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SK_ABI_VERSION 1
+#define SK_ABI_VERSION 2
 
 typedef enum sk_status {
     SK_OK = 0,
@@ -103,6 +103,18 @@ typedef struct sk_problem {
     int64_t k_stride_row, k_stride_head, k_stride_batch;
     int64_t v_stride_row, v_stride_head, v_stride_batch;
     int64_t o_stride_row, o_stride_head, o_stride_batch;
+    /* Optional device scratch for sk_attn_partial's load balance (or NULL).
+     * When the last round of workgroups would leave CUs idle, the items of
+     * that round are run as several workgroups over consecutive parts of
+     * their keys, whose results sk_attn_partial merges before it returns
+     * (the same log-sum-exp merge as sk_attn_combine).  The outputs then
+     * differ from whole items only by where the weights are rounded to bf16
+     * (each piece against its own running max).  It needs
+     * partial_scratch_bytes >= sk_partial_scratch_bytes(p), 16-byte
+     * alignment, and may not be shared by calls that can run at the same
+     * time.  NULL (or too small) runs every item whole. */
+    void* partial_scratch;
+    int64_t partial_scratch_bytes;
 } sk_problem;
 
 /* ABI version of the library (SK_ABI_VERSION of the header it was built from). */
@@ -120,6 +132,11 @@ int64_t sk_rows(const sk_problem* p);
 /* Bytes of the partial buffers sk_attn_partial writes and sk_attn_combine
  * reads (layout in the file header).  Either output pointer may be NULL. */
 sk_status sk_workspace_bytes(const sk_problem* p, size_t* o_part_bytes, size_t* lse_part_bytes);
+
+/* Bytes of partial_scratch that let sk_attn_partial balance its last round
+ * on the current device (0: the kernel selected for `p` never uses it), or
+ * -1 if `p` is invalid.  Depends on the device's CU count. */
+int64_t sk_partial_scratch_bytes(const sk_problem* p);
 
 /* Query rows per M block of the partial kernel selected for `p` (>= 1), or -1
  * if `p` is invalid or unsupported.  The kernel partitions each block's keys

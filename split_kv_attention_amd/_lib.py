@@ -24,6 +24,7 @@ EXPORTS = (
     "sk_status_string",
     "sk_rows",
     "sk_workspace_bytes",
+    "sk_partial_scratch_bytes",
     "sk_partial_m_per_block",
     "sk_valid_split_counts",
     "sk_attn_partial",
@@ -68,6 +69,8 @@ class SkProblem(ctypes.Structure):
         ("o_stride_row", ctypes.c_int64),
         ("o_stride_head", ctypes.c_int64),
         ("o_stride_batch", ctypes.c_int64),
+        ("partial_scratch", ctypes.c_void_p),
+        ("partial_scratch_bytes", ctypes.c_int64),
     ]
 
 
@@ -104,6 +107,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sk_rows.argtypes = [P]
     lib.sk_workspace_bytes.restype = ctypes.c_int
     lib.sk_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.sk_partial_scratch_bytes.restype = ctypes.c_int64
+    lib.sk_partial_scratch_bytes.argtypes = [P]
     lib.sk_partial_m_per_block.restype = ctypes.c_int32
     lib.sk_partial_m_per_block.argtypes = [P]
     lib.sk_valid_split_counts.restype = ctypes.c_int
@@ -169,6 +174,13 @@ def sk_workspace_bytes(problem: SkProblem) -> tuple[int, int]:
     l = ctypes.c_size_t(0)
     _check(load().sk_workspace_bytes(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(l)))
     return o.value, l.value
+
+
+def sk_partial_scratch_bytes(problem: SkProblem) -> int:
+    n = load().sk_partial_scratch_bytes(ctypes.byref(problem))
+    if n < 0:
+        raise SplitKVError(SK_ERR_INVALID_ARG, sk_last_error())
+    return n
 
 
 def sk_partial_m_per_block(problem: SkProblem) -> int:

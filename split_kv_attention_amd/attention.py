@@ -71,8 +71,11 @@ def build_problem(
     last_valid_per_seq=None,
     out_dtype: torch.dtype | None = None,
     out_strides: tuple[int, int, int] | None = None,
+    partial_scratch: bool = True,
 ) -> Problem:
-    """Describe one forward call; tensors stay where they are."""
+    """Describe one forward call; tensors stay where they are.  With
+    `partial_scratch` (and tensors on a GPU) the problem carries the scratch
+    buffer sk_attn_partial balances its last round of workgroups with."""
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
     dev = q.device
@@ -142,6 +145,13 @@ def build_problem(
         if t is not None:
             keep.append(t)
             setattr(p, name, t.data_ptr())
+    if partial_scratch and q.is_cuda:
+        nbytes = _lib.sk_partial_scratch_bytes(p)
+        if nbytes > 0:
+            scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            keep.append(scratch)
+            p.partial_scratch = scratch.data_ptr()
+            p.partial_scratch_bytes = nbytes
     return Problem(p, keep)
 
 

@@ -29,6 +29,8 @@
 //    with no visible key so far keeps m = -inf and zero weights.
 //  * Work items are remapped so each XCD streams one (head, split) key range
 //    through its own L2.
+#include <float.h>
+
 #include <type_traits>
 
 #include "sk_common.hpp"
@@ -151,7 +153,17 @@ void partial_bf16_kernel(PartialArgs a) {
     using C = Cfg<DQK, DV>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF_ELEMS];
 
-    const WorkItem it = decode_work(a);
+    // Workgroups past n_main run piece `piece` of tail item n_main + tail_i.
+    uint32_t item = blockIdx.x;
+    int piece = -1;
+    uint32_t tail_i = 0;
+    if (item >= a.n_main) {
+        const uint32_t j = item - a.n_main, n_tail = a.n_work - a.n_main;
+        tail_i = j % n_tail;
+        piece = (int)(j / n_tail);
+        item = a.n_main + tail_i;
+    }
+    const WorkItem it = decode_work(a, item);
     const Seq sq = load_seq(a.seqs, it.batch);
     if (it.split >= sq.splits) return;
     const int r0 = it.tile * kBM;
@@ -166,8 +178,15 @@ void partial_bf16_kernel(PartialArgs a) {
     // lastValid are never visible, so an empty key range (lastValid = -1)
     // gives an empty loop and no key is loaded.
     const int64_t kend = min(rl + 1, sq.lv + 1);
-    const int ks = (int)min((int64_t)it.split * kps, kend);
-    const int ke = (int)min((int64_t)(it.split + 1) * kps, kend);
+    int ks = (int)min((int64_t)it.split * kps, kend);
+    int ke = (int)min((int64_t)(it.split + 1) * kps, kend);
+    if (piece >= 0) {
+        // piece p of P takes key tiles [nt p / P, nt (p + 1) / P) of the split
+        const int nt = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
+        const int lo = (int)((int64_t)nt * piece / a.pieces), hi = (int)((int64_t)nt * (piece + 1) / a.pieces);
+        ke = min(ks + hi * kBN, ke);
+        ks = min(ks + lo * kBN, ke);
+    }
     // Smallest visibility limit in the block (its first row): tiles entirely
     // below it and inside the split need no per-element mask.
     const int64_t vis_first = vis_last(sq, mask, r0);
@@ -242,14 +261,22 @@ void partial_bf16_kernel(PartialArgs a) {
         const int rows = min(ke - kt, kBN);
         return rows > 0 ? (uint32_t)(((rows - 1) * row + d) * 2) : 0u;
     };
+    // K and V tiles are issued in key order: running source pointers.
+    const uint16_t* k_src = kbase + (int64_t)ks * a.k_row;
+    const uint16_t* v_src = vbase + (int64_t)ks * a.v_row;
+    const int64_t k_step = (int64_t)kBN * a.k_row, v_step = (int64_t)kBN * a.v_row;
+    const uint32_t k_full = (uint32_t)(((kBN - 1) * a.k_row + DQK) * 2);
+    const uint32_t v_full = (uint32_t)(((kBN - 1) * a.v_row + DV) * 2);
     auto issue_k = [&](int kt, int slot) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase + (int64_t)kt * a.k_row, tile_bytes(kt, a.k_row, DQK));
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(k_src, kt + kBN <= ke ? k_full : tile_bytes(kt, a.k_row, DQK));
+        k_src += k_step;
         uint16_t* dst = Ks0 + slot * C::K_ELEMS;
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i) load_lds16(r, k_off[i], dst + (i * kThreads + wave * 64) * 8);
     };
     auto issue_v = [&](int kt, int slot) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase + (int64_t)kt * a.v_row, tile_bytes(kt, a.v_row, DV));
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(v_src, kt + kBN <= ke ? v_full : tile_bytes(kt, a.v_row, DV));
+        v_src += v_step;
         uint16_t* dst = Vs0 + slot * C::V_ELEMS;
 #pragma unroll
         for (int i = 0; i < C::V_LOADS; ++i) load_lds16(r, v_off[i], dst + (i * kThreads + wave * 64) * 8);
@@ -402,17 +429,18 @@ void partial_bf16_kernel(PartialArgs a) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         if constexpr (step * kPairsPerStep < 16) {
-            float mc = mc_in;
-            asm volatile("" : "+v"(mc));  // keeps this slice below the step's wait
+            const float mc = mc_in;
 #pragma unroll
             for (int q = 0; q < kPairsPerStep; ++q) {
                 const int pr = step * kPairsPerStep + q;  // pair index 0..15
                 if (pr < 16) {
                     const int e = 2 * pr;  // element 0..31 = 16 kb + j
                     const int kb = e >> 4, j = e & 15;
+                    float x0 = fmaf(sacc[kb][j], cl2, -mc), x1 = fmaf(sacc[kb][j + 1], cl2, -mc);
+                    asm volatile("" : "+v"(x0), "+v"(x1));  // keeps this slice below the step's wait
                     bf16x2 p2;
-                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
-                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], cl2, -mc));
+                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(x0);
+                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(x1);
                     uint32_t packed = __builtin_bit_cast(uint32_t, p2);
                     asm volatile("" : "+v"(packed));  // keeps it above the next step's reads
                     p2 = __builtin_bit_cast(bf16x2, packed);
@@ -526,30 +554,94 @@ void partial_bf16_kernel(PartialArgs a) {
     const float l_tot = l_i + other_half(l_i);
     const bool empty = (m_i == -INFINITY);  // no visible key in this split
     const float inv = empty ? 0.f : 1.0f / l_tot;
-    const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
-    float* op = a.o_part + slot * DV + half * 4;
+    float* op;
+    float* lp;
+    if (piece < 0) {
+        const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+        op = a.o_part + slot * DV;
+        lp = a.lse_part + slot;
+    } else {
+        const int64_t slot = ((int64_t)tail_i * a.pieces + piece) * kBM + wave * 32 + col;
+        op = a.piece_o + slot * DV;
+        lp = a.piece_l + slot;
+    }
+    op += half * 4;
 #pragma unroll
     for (int c = 0; c < DV / 32; ++c)
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
             *reinterpret_cast<float4*>(op + c * 32 + jb * 8) =
                 make_float4(o[c][jb * 4] * inv, o[c][jb * 4 + 1] * inv, o[c][jb * 4 + 2] * inv, o[c][jb * 4 + 3] * inv);
-    if (half == 0) a.lse_part[slot] = empty ? -INFINITY : m_i * a.scale + logf(l_tot);
+    if (half == 0) *lp = empty ? -INFINITY : m_i * a.scale + logf(l_tot);
+}
+
+// Merge of the pieces of tail item n_main + blockIdx.x into its o_part /
+// lse_part slot: the pieces are a partition of the split's keys, so this is
+// the same log-sum-exp merge as the combine (rocmlirTriton page, "NaN-safe
+// merge"): m = max(max_p L_p, lowest finite), w_p = exp(L_p - m),
+// O_s = sum_p w_p O_p / max(sum_p w_p, 1), L_s = m + log(sum_p w_p), and a
+// row no piece saw any key of keeps (0, -inf).
+template <int DV>
+__global__ __launch_bounds__(kThreads) void merge_pieces_kernel(PartialArgs a) {
+    const uint32_t tail_i = blockIdx.x;
+    const WorkItem it = decode_work(a, a.n_main + tail_i);
+    const Seq sq = load_seq(a.seqs, it.batch);
+    if (it.split >= sq.splits) return;
+    const int r0 = it.tile * kBM;
+    if (r0 >= sq.sq) return;
+    const int nrows = min(kBM, sq.sq - r0);
+    constexpr int kParts = DV / 4;
+    const int P = a.pieces;
+    for (int t = threadIdx.x; t < nrows * kParts; t += kThreads) {
+        const int r = t / kParts, part = t - r * kParts;
+        const int64_t prow = sq.row0 + r0 + r;
+        if (prow >= a.rows) continue;
+        const int64_t base = (int64_t)tail_i * P * kBM + r;  // piece p: base + p * kBM
+        float m = -FLT_MAX;
+        for (int p = 0; p < P; ++p) m = fmaxf(m, a.piece_l[base + (int64_t)p * kBM]);
+        float den = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p = 0; p < P; ++p) {
+            const float w = expf(a.piece_l[base + (int64_t)p * kBM] - m);
+            const float4 x = *reinterpret_cast<const float4*>(a.piece_o + (base + (int64_t)p * kBM) * DV + part * 4);
+            den += w;
+            acc.x = fmaf(w, x.x, acc.x);
+            acc.y = fmaf(w, x.y, acc.y);
+            acc.z = fmaf(w, x.z, acc.z);
+            acc.w = fmaf(w, x.w, acc.w);
+        }
+        const float inv = 1.0f / fmaxf(den, 1.0f);
+        const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+        *reinterpret_cast<float4*>(a.o_part + slot * DV + part * 4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (part == 0) a.lse_part[slot] = den > 0.f ? m + logf(den) : -INFINITY;
+    }
 }
 
 template <int DQK, int DV>
 hipError_t launch(const PartialArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((partial_bf16_kernel<DQK, DV>), dim3(a.n_work), dim3(kThreads), 0, stream, a);
+    const uint32_t n_tail = a.n_work - a.n_main;
+    const uint32_t grid = a.n_main + n_tail * (uint32_t)a.pieces;
+    hipLaunchKernelGGL((partial_bf16_kernel<DQK, DV>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (n_tail > 0) hipLaunchKernelGGL((merge_pieces_kernel<DV>), dim3(n_tail), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int DQK, int DV>
+int blocks_per_cu() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<DQK, DV>, kThreads, 0) != hipSuccess)
+        return 0;
+    return n;
 }
 
 }  // namespace
 
 PartialKernel find_partial_bf16(int d_qk, int d_v) {
-    if (d_qk == 64 && d_v == 64) return {launch<64, 64>, kBM};
-    if (d_qk == 128 && d_v == 128) return {launch<128, 128>, kBM};
-    if (d_qk == 192 && d_v == 128) return {launch<192, 128>, kBM};
-    return {nullptr, 0};
+    if (d_qk == 64 && d_v == 64) return {launch<64, 64>, kBM, blocks_per_cu<64, 64>};
+    if (d_qk == 128 && d_v == 128) return {launch<128, 128>, kBM, blocks_per_cu<128, 128>};
+    if (d_qk == 192 && d_v == 128) return {launch<192, 128>, kBM, blocks_per_cu<192, 128>};
+    return {nullptr, 0, nullptr};
 }
 
 }  // namespace sk

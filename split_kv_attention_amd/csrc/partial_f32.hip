@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
     __shared__ float4 Ks[BN * DQK / 4];
     __shared__ float4 Vs[BN * DV / 4];
 
-    const WorkItem it = decode_work(a);
+    const WorkItem it = decode_work(a, blockIdx.x);
     const Seq sq = load_seq(a.seqs, it.batch);
     if (it.split >= sq.splits) return;
     const int r0 = it.tile * kF32Rows;
@@ -156,11 +156,11 @@ hipError_t launch(const PartialArgs& a, hipStream_t stream) {
 }  // namespace
 
 PartialKernel find_partial_f32(int d_qk, int d_v) {
-    if (d_qk == 16 && d_v == 16) return {launch<16, 16, 32>, kF32Rows};
-    if (d_qk == 32 && d_v == 32) return {launch<32, 32, 32>, kF32Rows};
-    if (d_qk == 64 && d_v == 64) return {launch<64, 64, 32>, kF32Rows};
-    if (d_qk == 128 && d_v == 128) return {launch<128, 128, 16>, kF32Rows};
-    return {nullptr, 0};
+    if (d_qk == 16 && d_v == 16) return {launch<16, 16, 32>, kF32Rows, nullptr};
+    if (d_qk == 32 && d_v == 32) return {launch<32, 32, 32>, kF32Rows, nullptr};
+    if (d_qk == 64 && d_v == 64) return {launch<64, 64, 32>, kF32Rows, nullptr};
+    if (d_qk == 128 && d_v == 128) return {launch<128, 128, 16>, kF32Rows, nullptr};
+    return {nullptr, 0, nullptr};
 }
 
 }  // namespace sk

@@ -106,6 +106,17 @@ struct PartialArgs {
     uint32_t n_work;   // n_tiles * heads * split_kv * batch
     float scale;       // softmax scale
     float scale_log2;  // softmax scale * log2(e)
+    // Tail split (load balance of the last round): work items n_main ..
+    // n_work - 1 are each run as `pieces` workgroups over consecutive parts
+    // of their key range, which write to the scratch arrays
+    //   piece_o [n_work - n_main][pieces][m_per_block][D_v]
+    //   piece_l [n_work - n_main][pieces][m_per_block]
+    // and a merge kernel folds the pieces into o_part / lse_part.  With
+    // n_main = n_work (pieces = 1) every item runs whole.
+    uint32_t n_main;
+    int32_t pieces;
+    float* piece_o;
+    float* piece_l;
 };
 
 // Decoded work item of a partial kernel.
@@ -146,16 +157,16 @@ __device__ __forceinline__ uint32_t pair_by_rank(const PartialArgs& a, uint32_t 
     return hit ? (uint32_t)__builtin_ctzll(hit) : r;
 }
 
-// Work items are groups (pair, head) of n_tiles query tiles each; groups are
+// Work item b in [0, n_work): groups (pair, head) of n_tiles query tiles each; groups are
 // ordered longest pair first.  Workgroups are dealt round-robin over the 8
 // XCDs of an MI355X (XCD = blockIdx.x % 8), so block b is mapped to give XCD x
 // the groups x, x + 8, x + 16, ... in that order: every XCD gets an equal
 // share of long and short groups, runs its longest first, and the tiles of
 // one group (which read the same keys and values) share its L2.  Groups past
 // the last multiple of 8 are spread tile by tile.  A bijection on [0, n_work).
-__device__ __forceinline__ WorkItem decode_work(const PartialArgs& a) {
+__device__ __forceinline__ WorkItem decode_work(const PartialArgs& a, uint32_t b) {
     constexpr uint32_t kXcds = 8;
-    const uint32_t T = a.n_tiles, G = a.n_work / T, b = blockIdx.x;
+    const uint32_t T = a.n_tiles, G = a.n_work / T;
     uint32_t u = b;
     if (b < (G / kXcds) * kXcds * T) {
         const uint32_t x = b % kXcds, i = b / kXcds;
@@ -201,6 +212,9 @@ typedef hipError_t (*PartialLauncher)(const PartialArgs& a, hipStream_t stream);
 struct PartialKernel {
     PartialLauncher launch;
     int m_per_block;
+    // Workgroups of the kernel resident per CU (for the tail split), or
+    // nullptr when the kernel runs every item whole.
+    int (*blocks_per_cu)();
 };
 // Kernel for (dtype, d_qk, d_v), or {nullptr, 0} when not built.
 PartialKernel find_partial_bf16(int d_qk, int d_v);

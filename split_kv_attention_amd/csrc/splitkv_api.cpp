@@ -3,6 +3,8 @@
 // frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -66,6 +68,7 @@ sk_status check_problem(const sk_problem* p) {
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
         return fail(SK_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
     if (p->reserved0 != 0) return fail(SK_ERR_INVALID_ARG, "reserved0 must be 0");
+    if (p->partial_scratch_bytes < 0) return fail(SK_ERR_INVALID_ARG, "partial_scratch_bytes must be >= 0");
     const int64_t strides[] = {p->q_stride_row, p->q_stride_head, p->q_stride_batch, p->k_stride_row,
                                p->k_stride_head, p->k_stride_batch, p->v_stride_row, p->v_stride_head,
                                p->v_stride_batch, p->o_stride_row, p->o_stride_head, p->o_stride_batch};
@@ -99,6 +102,56 @@ bool aligned(const void* ptr, size_t bytes) { return ((uintptr_t)ptr % bytes) ==
 sk::PartialKernel pick_partial(const sk_problem& p) {
     return p.dtype == SK_BF16 ? sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v)
                               : sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of the partial kernel resident on the device at once (0 when
+// unknown or when the kernel runs every item whole).
+int64_t partial_slots(const sk::PartialKernel& k) {
+    if (!k.blocks_per_cu) return 0;
+    return (int64_t)k.blocks_per_cu() * cu_count();
+}
+
+int64_t piece_scratch_bytes(int64_t items, int64_t m_per_block, int64_t dv) {
+    return items * m_per_block * (dv + 1) * (int64_t)sizeof(float);
+}
+
+// Tail split: the last round of a launch holds n_work mod slots items (all
+// of them when n_work < slots).  Each is cut into as many key pieces as keep
+// every slot busy, with at least kMinPieceTiles key tiles of 64 per piece
+// (by the longest sequence's split) and at most kMaxPieces.
+struct TailPlan {
+    uint32_t n_main;
+    int pieces;
+};
+TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_work) {
+    constexpr int64_t kMinPieceTiles = 8, kMaxPieces = 16;
+    TailPlan none{(uint32_t)n_work, 1};
+    const int64_t slots = partial_slots(k);
+    if (slots <= 0 || !p.partial_scratch) return none;
+    const int64_t tail = n_work % slots;
+    if (tail == 0) return none;
+    const int64_t split_keys = ((int64_t)p.max_seqlen_k + p.split_kv - 1) / p.split_kv;
+    const int64_t tiles = (split_keys + 63) / 64;
+    const int64_t pieces = std::min({slots / tail, tiles / kMinPieceTiles, kMaxPieces});
+    if (pieces < 2) return none;
+    if (piece_scratch_bytes(tail * pieces, k.m_per_block, p.head_dim_v) > p.partial_scratch_bytes) return none;
+    return TailPlan{(uint32_t)(n_work - tail), (int)pieces};
 }
 
 sk_status hip_status(hipError_t e, const char* what) {
@@ -136,6 +189,14 @@ sk_status sk_workspace_bytes(const sk_problem* p, size_t* o_part_bytes, size_t* 
     if (o_part_bytes) *o_part_bytes = slots * p->head_dim_v * sizeof(float);
     if (lse_part_bytes) *lse_part_bytes = slots * sizeof(float);
     return ok();
+}
+
+int64_t sk_partial_scratch_bytes(const sk_problem* p) {
+    if (check_problem(p) != SK_OK) return -1;
+    const sk::PartialKernel k = pick_partial(*p);
+    const int64_t slots = k.launch ? partial_slots(k) : 0;
+    ok();
+    return slots > 0 ? piece_scratch_bytes(slots, k.m_per_block, p->head_dim_v) : 0;
 }
 
 int32_t sk_partial_m_per_block(const sk_problem* p) {
@@ -211,6 +272,18 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
     a.n_work = (uint32_t)n_work;
     a.scale = p->softmax_scale;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    if (p->partial_scratch && !aligned(p->partial_scratch, 16))
+        return fail(SK_ERR_INVALID_ARG, "partial_scratch must be 16-byte aligned");
+    const TailPlan plan = plan_tail(*p, kern, n_work);
+    a.n_main = plan.n_main;
+    a.pieces = plan.pieces;
+    a.piece_o = nullptr;
+    a.piece_l = nullptr;
+    if (plan.pieces > 1) {
+        const int64_t piece_rows = (n_work - plan.n_main) * (int64_t)plan.pieces * kern.m_per_block;
+        a.piece_o = static_cast<float*>(p->partial_scratch);
+        a.piece_l = a.piece_o + piece_rows * p->head_dim_v;
+    }
     return hip_status(kern.launch(a, (hipStream_t)stream), "partial kernel launch");
 }
 

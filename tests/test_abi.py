@@ -23,7 +23,8 @@ def _declared_functions():
 
 def test_library_builds_and_loads():
     lib = _lib.load()
-    assert lib.sk_abi_version() == 1
+    version = int(re.search(r"#define SK_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.sk_abi_version() == version
 
 
 def test_every_declared_function_is_exported():
@@ -111,6 +112,7 @@ BAD = [
     ("head_dim_v", 512, sk.SK_ERR_UNSUPPORTED),
     ("reserved0", 1, sk.SK_ERR_INVALID_ARG),
     ("k_stride_row", -8, sk.SK_ERR_INVALID_ARG),
+    ("partial_scratch_bytes", -1, sk.SK_ERR_INVALID_ARG),
 ]
 
 
@@ -148,6 +150,19 @@ def test_unsupported_layouts_are_rejected():
     p = _good()
     p.head_dim_v = 126
     assert lib.sk_attn_combine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == sk.SK_ERR_UNSUPPORTED
+
+
+def test_partial_scratch_checks():
+    lib = _lib.load()
+    p = _good()
+    assert lib.sk_partial_scratch_bytes(ctypes.byref(p)) >= 0  # 0 without a GPU
+    p.num_heads = 0
+    assert lib.sk_partial_scratch_bytes(ctypes.byref(p)) == -1
+    p = _good()
+    p.partial_scratch = FAKE + 4  # not 16-byte aligned
+    p.partial_scratch_bytes = 1 << 20
+    assert lib.sk_attn_partial(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == sk.SK_ERR_INVALID_ARG
+    assert "aligned" in sk.sk_last_error()
 
 
 def test_empty_problems_are_no_ops():

@@ -137,6 +137,47 @@ SMALL = [
 ]
 
 
+# Few work items against many resident workgroups with long splits: the
+# partial kernel runs these items as several key pieces and merges them
+# (load balance of the last round).  Masks leave whole pieces empty for some
+# rows, and short sequences get fewer key tiles than pieces.
+TAIL = [
+    _shrink(workloads.LONG_PREFILL, name="tail_split_H2_Sq256_Sk8192_S2", heads=2, sq=(256,), sk=(8192,), split_kv=2),
+    _shrink(workloads.LONG_PREFILL, name="tail_split_prefix_H3_Sq300_Sk9000_S3", heads=3, sq=(300,), sk=(9000,),
+            split_kv=3, mask="prefix_causal", prefix_offset_per_seq=(8100,), last_valid_per_seq=(8899,)),
+    _shrink(workloads.VARLEN_BATCH, name="tail_split_varlen_short_seqs", heads=2, sq=(130, 1, 64, 0, 200),
+            sk=(12000, 100, 7000, 50, 3), split_kv=4, split_kv_per_seq=(4, 1, 3, 2, 4)),
+    _shrink(workloads.CAUSAL_BF16, name="tail_split_dense_bottom_right_d128", heads=2, sq=(200, 200),
+            sk=(6000, 6000), split_kv=2, mask="prefix_causal", prefix_offset=5800),
+]
+
+
+@pytest.mark.parametrize("w", TAIL, ids=lambda w: w.name)
+def test_tail_split_all_rows(w):
+    log(f"tail {w.name}")
+    inputs, prob, res = run_gpu(w, seed=5)
+    assert prob.c.partial_scratch and prob.c.partial_scratch_bytes > 0
+    st = compare(w, inputs, prob, res, label=w.name)
+    log(f"  {st}")
+    # the same problem without scratch runs every item whole
+    from split_kv_attention_amd import attention
+    prob2 = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], partial_scratch=False,
+                                    **workloads.problem_kwargs(w, inputs))
+    o2 = torch.full_like(res["o_part"], float("nan"))
+    l2 = torch.full_like(res["lse_part"], float("nan"))
+    from split_kv_attention_amd import _lib
+    _lib.sk_attn_partial(prob2.c, inputs["q"], inputs["k"], inputs["v"], o2, l2)
+    torch.cuda.synchronize()
+    written = ~torch.isnan(res["o_part"])
+    assert torch.equal(written, ~torch.isnan(o2))
+    assert torch.equal(torch.isneginf(res["lse_part"]), torch.isneginf(l2))
+    # pieces round their weights to bf16 against their own running max, so
+    # the two runs differ by the weights' rounding, far inside the tolerance
+    assert (res["o_part"][written] - o2[written]).abs().max().item() < 2e-3
+    fin = torch.isfinite(l2)
+    assert (res["lse_part"][fin] - l2[fin]).abs().max().item() < 2e-3
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_small_cases_all_rows(w):
     log(f"e2e {w.name}")
