@@ -26,7 +26,9 @@ METRIC = "attention TFLOP/s (% bf16 MFMA peak) at Sq4096 Sk42700 H12; combine GB
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_hbm_traffic.json")
-PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/sk_common.hpp"]
+# the partial entry point's kernels and the host code that plans their launch
+PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/sk_common.hpp",
+                   "split_kv_attention_amd/csrc/splitkv_api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -202,7 +204,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "partial_bf16_kernel<192,128>",
+            "kernel": "sk_attn_partial (partial_bf16_kernel<192,128>, then merge_pieces_kernel<128> for the "
+                      "last round's key pieces)",
             "kernel_ms": t_partial,
             "algorithmic_flop": flops,
             "algorithmic_bytes": partial_bytes,

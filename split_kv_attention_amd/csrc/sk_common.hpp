@@ -89,6 +89,9 @@ __device__ __forceinline__ int32_t valid_split_count(const Seq& s, int mask, int
     return (int32_t)ceil_div64(rl + 1, keys_per_split(rl, n_per_block, s.splits));
 }
 
+// Most key pieces one tail item of the partial kernel is split into.
+constexpr int kMaxPieces = 16;
+
 // Arguments of every partial-attention kernel.
 struct PartialArgs {
     const void* q;
@@ -114,7 +117,7 @@ struct PartialArgs {
     // and a merge kernel folds the pieces into o_part / lse_part.  With
     // n_main = n_work (pieces = 1) every item runs whole.
     uint32_t n_main;
-    int32_t pieces;
+    int32_t pieces;    // 2 .. kMaxPieces when n_main < n_work
     float* piece_o;
     float* piece_l;
 };

@@ -134,13 +134,13 @@ int64_t piece_scratch_bytes(int64_t items, int64_t m_per_block, int64_t dv) {
 // Tail split: the last round of a launch holds n_work mod slots items (all
 // of them when n_work < slots).  Each is cut into as many key pieces as keep
 // every slot busy, with at least kMinPieceTiles key tiles of 64 per piece
-// (by the longest sequence's split) and at most kMaxPieces.
+// (by the longest sequence's split) and at most sk::kMaxPieces.
 struct TailPlan {
     uint32_t n_main;
     int pieces;
 };
 TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_work) {
-    constexpr int64_t kMinPieceTiles = 8, kMaxPieces = 16;
+    constexpr int64_t kMinPieceTiles = 8;
     TailPlan none{(uint32_t)n_work, 1};
     const int64_t slots = partial_slots(k);
     if (slots <= 0 || !p.partial_scratch) return none;
@@ -148,7 +148,7 @@ TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_wo
     if (tail == 0) return none;
     const int64_t split_keys = ((int64_t)p.max_seqlen_k + p.split_kv - 1) / p.split_kv;
     const int64_t tiles = (split_keys + 63) / 64;
-    const int64_t pieces = std::min({slots / tail, tiles / kMinPieceTiles, kMaxPieces});
+    const int64_t pieces = std::min({slots / tail, tiles / kMinPieceTiles, (int64_t)sk::kMaxPieces});
     if (pieces < 2) return none;
     if (piece_scratch_bytes(tail * pieces, k.m_per_block, p.head_dim_v) > p.partial_scratch_bytes) return none;
     return TailPlan{(uint32_t)(n_work - tail), (int)pieces};
