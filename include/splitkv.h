@@ -31,8 +31,9 @@
  * it (dense batch) it is b * max_seqlen_q + r.  sk_rows() returns their number.
  *
  * Partial buffers (written by sk_attn_partial, read by sk_attn_combine), f32:
- *   o_part   [num_heads][split_kv][rows][head_dim_v]
- *   lse_part [num_heads][split_kv][rows]
+ *   o_part   [num_heads][S_max][rows][head_dim_v]
+ *   lse_part [num_heads][S_max][rows]
+ * with S_max = sk_split_kv(p) (split_kv unless split_kv = 0).
  * i.e. the split axis sits right after the batch-head axis, as in the per-row
  * mask layout of the rocmlirTriton page ("Per-row mask layout").
  */
@@ -82,7 +83,8 @@ typedef struct sk_problem {
     int32_t head_dim_qk;    /* D_qk */
     int32_t head_dim_v;     /* D_v */
     int32_t split_kv;       /* S_max >= 1: splits per (sequence, head); 1 = unsplit
-                               (aiter page: num_splits 2..8 force a split) */
+                               (aiter page: num_splits 2..8 force a split);
+                               0 = automatic, see sk_split_kv() */
     int32_t n_per_block;    /* split granularity in keys (>= 1): the key tile
                                nPerBlock of the count formula */
     int32_t mask;           /* sk_mask_mode */
@@ -94,7 +96,8 @@ typedef struct sk_problem {
     int32_t reserved0;      /* must be 0 */
     const int32_t* cu_seqlens_q;          /* device [B+1] prefix sums, or NULL = dense */
     const int32_t* cu_seqlens_k;          /* device [B+1] prefix sums, or NULL = dense */
-    const int32_t* split_kv_per_seq;      /* device [B], each in 1..split_kv, or NULL */
+    const int32_t* split_kv_per_seq;      /* device [B], each in 1..split_kv, or NULL
+                                             (must be NULL when split_kv = 0) */
     const int32_t* prefix_offset_per_seq; /* device [B] (PREFIX_CAUSAL), or NULL */
     const int32_t* last_valid_per_seq;    /* device [B] (< 0: Sk_b - 1), or NULL */
     /* Element strides.  The head dimension is contiguous (stride 1).  The batch
@@ -128,6 +131,22 @@ const char* sk_status_string(sk_status status);
 
 /* Number of packed query rows (see "Row numbering"), or -1 if `p` is invalid. */
 int64_t sk_rows(const sk_problem* p);
+
+/* The number of splits S_max every entry point uses for `p` (>= 1), or -1 if
+ * `p` is invalid.  It is split_kv, or with split_kv = 0 the automatic choice
+ * (aiter page, Technical Details: split only when the keys are long and the
+ * query tiles alone do not fill the GPU), re-derived for this device:
+ *   items = query tiles of 128 rows x heads (batch x tiles of the longest
+ *           sequence, or for a packed batch at most ceil(total_q / 128) + B - 1)
+ *   slots = resident workgroups of the bf16 partial kernel (2 per CU)
+ *   S     = clamp(round(slots / items), 2, 8)  if max_seqlen_k >= 8192 and
+ *           items <= slots, else 1.
+ * The key threshold is the explicit 8192 of that page's contract (its review
+ * notes a tile-rounded form that also split 8161..8191 keys).  f32 problems
+ * and head dims without a bf16 kernel stay unsplit.  The result depends on
+ * the current device's CU count, so buffers must be sized with the same
+ * device current. */
+int32_t sk_split_kv(const sk_problem* p);
 
 /* Bytes of the partial buffers sk_attn_partial writes and sk_attn_combine
  * reads (layout in the file header).  Either output pointer may be NULL. */

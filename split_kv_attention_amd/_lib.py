@@ -23,6 +23,7 @@ EXPORTS = (
     "sk_last_error",
     "sk_status_string",
     "sk_rows",
+    "sk_split_kv",
     "sk_workspace_bytes",
     "sk_partial_scratch_bytes",
     "sk_partial_m_per_block",
@@ -105,6 +106,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_rows.restype = ctypes.c_int64
     lib.sk_rows.argtypes = [P]
+    lib.sk_split_kv.restype = ctypes.c_int32
+    lib.sk_split_kv.argtypes = [P]
     lib.sk_workspace_bytes.restype = ctypes.c_int
     lib.sk_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.sk_partial_scratch_bytes.restype = ctypes.c_int64
@@ -174,6 +177,13 @@ def sk_workspace_bytes(problem: SkProblem) -> tuple[int, int]:
     l = ctypes.c_size_t(0)
     _check(load().sk_workspace_bytes(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(l)))
     return o.value, l.value
+
+
+def sk_split_kv(problem: SkProblem) -> int:
+    n = load().sk_split_kv(ctypes.byref(problem))
+    if n < 0:
+        raise SplitKVError(SK_ERR_INVALID_ARG, sk_last_error())
+    return n
 
 
 def sk_partial_scratch_bytes(problem: SkProblem) -> int:

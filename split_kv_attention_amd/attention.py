@@ -34,6 +34,11 @@ class Problem:
         return _lib.sk_rows(self.c)
 
     @property
+    def split_kv(self) -> int:
+        """Splits the library uses (the automatic count when split_kv = 0)."""
+        return _lib.sk_split_kv(self.c)
+
+    @property
     def m_per_block(self) -> int:
         return _lib.sk_partial_m_per_block(self.c)
 
@@ -161,8 +166,9 @@ def alloc_outputs(prob: Problem, q: torch.Tensor, v: torch.Tensor, out_dtype: to
     dev = q.device
     rows = prob.rows
     counts = torch.empty(rows, dtype=torch.int32, device=dev)
-    o_part = torch.empty((c.num_heads, c.split_kv, rows, c.head_dim_v), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((c.num_heads, c.split_kv, rows), dtype=torch.float32, device=dev)
+    s_max = prob.split_kv
+    o_part = torch.empty((c.num_heads, s_max, rows, c.head_dim_v), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((c.num_heads, s_max, rows), dtype=torch.float32, device=dev)
     od = out_dtype or q.dtype
     if q.dim() == 4:
         out = torch.empty((c.batch, c.num_heads, c.max_seqlen_q, c.head_dim_v), dtype=od, device=dev)

@@ -31,6 +31,7 @@
 //    through its own L2.
 #include <float.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "sk_common.hpp"
@@ -646,11 +647,15 @@ hipError_t launch(const PartialArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Resident workgroups per CU (the same on every gfx950 device; cached).
 template <int DQK, int DV>
 int blocks_per_cu() {
-    int n = 0;
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n > 0) return n;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<DQK, DV>, kThreads, 0) != hipSuccess)
         return 0;
+    cached.store(n, std::memory_order_relaxed);
     return n;
 }
 

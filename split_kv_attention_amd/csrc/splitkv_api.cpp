@@ -56,7 +56,9 @@ sk_status check_problem(const sk_problem* p) {
     if (p->head_dim_qk > kMaxHeadDim || p->head_dim_v > kMaxHeadDim)
         return fail(SK_ERR_UNSUPPORTED, "head dims above %d are not supported (got %d, %d)", kMaxHeadDim,
                     p->head_dim_qk, p->head_dim_v);
-    if (p->split_kv < 1) return fail(SK_ERR_INVALID_ARG, "split_kv must be >= 1 (got %d)", p->split_kv);
+    if (p->split_kv < 0) return fail(SK_ERR_INVALID_ARG, "split_kv must be >= 0 (got %d)", p->split_kv);
+    if (p->split_kv == 0 && p->split_kv_per_seq)
+        return fail(SK_ERR_INVALID_ARG, "split_kv_per_seq needs an explicit split_kv (got 0 = automatic)");
     if (p->split_kv > kMaxSplits)
         return fail(SK_ERR_UNSUPPORTED, "split_kv above %d is not supported (got %d)", kMaxSplits, p->split_kv);
     if (p->n_per_block < 1) return fail(SK_ERR_INVALID_ARG, "n_per_block must be >= 1 (got %d)", p->n_per_block);
@@ -154,6 +156,31 @@ TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_wo
     return TailPlan{(uint32_t)(n_work - tail), (int)pieces};
 }
 
+// Automatic split count for split_kv = 0 (documented with sk_split_kv).
+int32_t auto_split_kv(const sk_problem& p) {
+    constexpr int64_t kMinKeys = 8192;
+    constexpr int64_t kMaxAutoSplits = 8;
+    if (p.max_seqlen_k < kMinKeys) return 1;
+    sk_problem q = p;
+    q.split_kv = 1;
+    const sk::PartialKernel k = pick_partial(q);
+    if (!k.launch || p.dtype != SK_BF16) return 1;
+    const int64_t slots = partial_slots(k);
+    const int64_t mpb = k.m_per_block;
+    int64_t tiles = (int64_t)p.batch * ((p.max_seqlen_q + mpb - 1) / mpb);
+    if (p.cu_seqlens_q) tiles = std::min(tiles, ((int64_t)p.total_q + mpb - 1) / mpb + p.batch - 1);
+    const int64_t items = tiles * p.num_heads;
+    if (slots <= 0 || items <= 0 || items > slots) return 1;
+    return (int32_t)std::clamp((slots + items / 2) / items, (int64_t)2, kMaxAutoSplits);
+}
+
+// The problem with split_kv resolved (split_kv = 0 -> the automatic count).
+sk_problem resolved(const sk_problem& p) {
+    sk_problem r = p;
+    if (r.split_kv == 0) r.split_kv = auto_split_kv(p);
+    return r;
+}
+
 sk_status hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(SK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -185,10 +212,18 @@ int64_t sk_rows(const sk_problem* p) {
 sk_status sk_workspace_bytes(const sk_problem* p, size_t* o_part_bytes, size_t* lse_part_bytes) {
     sk_status st = check_problem(p);
     if (st != SK_OK) return st;
+    const sk_problem rp = resolved(*p);
+    p = &rp;
     const size_t slots = (size_t)p->num_heads * p->split_kv * (size_t)rows_of(*p);
     if (o_part_bytes) *o_part_bytes = slots * p->head_dim_v * sizeof(float);
     if (lse_part_bytes) *lse_part_bytes = slots * sizeof(float);
     return ok();
+}
+
+int32_t sk_split_kv(const sk_problem* p) {
+    if (check_problem(p) != SK_OK) return -1;
+    ok();
+    return resolved(*p).split_kv;
 }
 
 int64_t sk_partial_scratch_bytes(const sk_problem* p) {
@@ -214,6 +249,8 @@ int32_t sk_partial_m_per_block(const sk_problem* p) {
 sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stream) {
     sk_status st = check_problem(p);
     if (st != SK_OK) return st;
+    const sk_problem rp = resolved(*p);
+    p = &rp;
     if (p->batch == 0 || p->max_seqlen_q == 0 || rows_of(*p) == 0) return ok();
     if (!counts) return fail(SK_ERR_INVALID_ARG, "counts is NULL");
     sk::CountsArgs a;
@@ -226,6 +263,8 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
                           float* lse_part, void* stream) {
     sk_status st = check_problem(p);
     if (st != SK_OK) return st;
+    const sk_problem rp = resolved(*p);
+    p = &rp;
     const sk::PartialKernel kern = pick_partial(*p);
     if (!kern.launch)
         return fail(SK_ERR_UNSUPPORTED, "no partial kernel for dtype %s with head dims (%d, %d)",
@@ -291,6 +330,8 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
                           void* out, float* lse_out, void* stream) {
     sk_status st = check_problem(p);
     if (st != SK_OK) return st;
+    const sk_problem rp = resolved(*p);
+    p = &rp;
     const int64_t rows = rows_of(*p);
     if (p->batch == 0 || p->max_seqlen_q == 0 || rows == 0) return ok();
     if (!o_part || !lse_part || !out) return fail(SK_ERR_INVALID_ARG, "o_part, lse_part and out must not be NULL");

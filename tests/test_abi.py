@@ -99,7 +99,7 @@ BAD = [
     ("num_heads", 0, sk.SK_ERR_INVALID_ARG),
     ("batch", -1, sk.SK_ERR_INVALID_ARG),
     ("max_seqlen_q", -5, sk.SK_ERR_INVALID_ARG),
-    ("split_kv", 0, sk.SK_ERR_INVALID_ARG),
+    ("split_kv", -1, sk.SK_ERR_INVALID_ARG),
     ("split_kv", 1000, sk.SK_ERR_UNSUPPORTED),
     ("n_per_block", 0, sk.SK_ERR_INVALID_ARG),
     ("mask", 7, sk.SK_ERR_INVALID_ARG),
@@ -152,6 +152,21 @@ def test_unsupported_layouts_are_rejected():
     assert lib.sk_attn_combine(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == sk.SK_ERR_UNSUPPORTED
 
 
+def test_automatic_split_count_on_the_host():
+    lib = _lib.load()
+    p = _good()
+    assert lib.sk_split_kv(ctypes.byref(p)) == p.split_kv  # explicit counts pass through
+    p.split_kv = 0
+    n = lib.sk_split_kv(ctypes.byref(p))
+    assert 1 <= n <= 8  # 1 without a GPU (no CU count to fill)
+    p.max_seqlen_k = 8191  # below the key threshold: unsplit on any device
+    assert lib.sk_split_kv(ctypes.byref(p)) == 1
+    p.split_kv_per_seq = FAKE  # per-sequence counts need an explicit maximum
+    assert lib.sk_split_kv(ctypes.byref(p)) == -1
+    assert lib.sk_attn_partial(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == sk.SK_ERR_INVALID_ARG
+    assert "split_kv_per_seq" in sk.sk_last_error()
+
+
 def test_partial_scratch_checks():
     lib = _lib.load()
     p = _good()
@@ -189,6 +204,6 @@ def test_binding_raises_without_the_library(tmp_path):
 
 def test_split_kv_error_carries_the_message():
     p = _good()
-    p.split_kv = 0
+    p.split_kv = -2
     with pytest.raises(sk.SplitKVError, match="split_kv"):
         sk.sk_valid_split_counts(p, FAKE, 0)

@@ -178,6 +178,42 @@ def test_tail_split_all_rows(w):
     assert (res["lse_part"][fin] - l2[fin]).abs().max().item() < 2e-3
 
 
+def test_automatic_split_count_both_sides_of_the_thresholds():
+    """split_kv = 0: unsplit below 8192 keys or when the query tiles alone
+    fill the GPU, else clamp(round(slots / items), 2, 8) splits."""
+    from split_kv_attention_amd import attention
+
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count  # two workgroups per CU
+
+    def auto(sq, sk, dtype="bf16"):
+        w = _shrink(workloads.LONG_PREFILL, sq=(sq,), sk=(sk,), split_kv=0, dtype=dtype)
+        inputs = workloads.make_inputs(w, DEV, seed=0)
+        prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+        return prob.split_kv
+
+    def rule(items):
+        return max(2, min(8, (slots + items // 2) // items)) if items <= slots else 1
+
+    assert auto(1024, 8191) == 1  # one key below the threshold (the page's tile-rounded form split here)
+    assert auto(1024, 8192) == rule(12 * 8) > 1
+    assert auto(4096, 42700) == rule(12 * 32)
+    assert auto(8192, 16384) == (rule(12 * 64) if 12 * 64 <= slots else 1)
+    assert auto(1024, 8192, dtype="f32") == 1  # no bf16 MFMA kernel contract
+
+
+def test_automatic_split_end_to_end():
+    """The resolved count drives every entry point; results match the oracle
+    run with that count."""
+    w = _shrink(workloads.LONG_PREFILL, name="auto_split_Sq1024_Sk8192", sq=(1024,), sk=(8192,), split_kv=0)
+    log(f"auto {w.name}")
+    inputs, prob, res = run_gpu(w, seed=7)
+    S = prob.split_kv
+    assert S > 1 and res["o_part"].shape[1] == S
+    rows = {0: sample_rows(1024, 48, seed=0, tile=prob.m_per_block)}
+    st = compare(_shrink(w, split_kv=S), inputs, prob, res, rows_per_seq=rows, label=w.name)
+    log(f"  S={S} {st}")
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_small_cases_all_rows(w):
     log(f"e2e {w.name}")
