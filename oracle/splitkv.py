@@ -282,6 +282,22 @@ def kernel_nonempty_splits(spec: SeqSpec, m_per_block: int, row: int) -> int:
     return n
 
 
+def block_populated_splits(spec: SeqSpec, m_per_block: int, row: int) -> int:
+    """Number of splits of `row`'s query block whose key range holds a key
+    that exists (index <= lastValid).  These are the splits a kernel with
+    real early exit still writes [R, the review note on real early exit: a
+    workgroup with no work exits without writing, and the host side must then
+    stop assuming those slots are initialised]; every other split of the
+    block is (0, -inf) for all its rows, so a merge may leave it out.
+    """
+    lv = spec.last_valid_index
+    n = 0
+    for a, b in block_split_ranges(spec, m_per_block, row // m_per_block):
+        if b > a and a <= lv:
+            n += 1
+    return n
+
+
 __all__ = [
     "MASK_NONE",
     "MASK_CAUSAL",
@@ -299,4 +315,5 @@ __all__ = [
     "split_attention",
     "visible_pairs",
     "kernel_nonempty_splits",
+    "block_populated_splits",
 ]

@@ -136,7 +136,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         }
     }
     int c = a.counts ? a.counts[row] : valid_split_count(s, a.seqs.mask, a.seqs.n_per_block, r);
-    c = min(max(c, 0), S_b);  // never read a split the partial kernel did not write
+    c = min(max(c, 0), S_b);
+    // Splits past the ones the row's M block populates were not written
+    // (they hold no key for the block, so their weight would be 0).  Without
+    // a mask every row of a sequence has the same last visible key, so the
+    // populated count equals the count, except for a sequence with no key
+    // (count 1, nothing populated).  A packed block's rows lie in one M block
+    // (rows_per_block divides the M block), so the cap is computed once,
+    // from the block's first row.
+    if (a.m_per_block > 0) {
+        if (a.seqs.mask == SK_MASK_NONE) {
+            if (s.lv < 0) c = 0;
+        } else {
+            c = min(c, block_populated_splits(s, a.seqs.mask, a.seqs.n_per_block, a.m_per_block,
+                                              kPacked && a.m_per_block % rows_per_block == 0 ? (int)blk : r));
+        }
+    }
 
     // m = max(max_s L_s, lowest finite); w_s = exp(L_s - m);
     // O = sum_s w_s O_s / max(sum_s w_s, 1)

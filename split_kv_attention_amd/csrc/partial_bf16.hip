@@ -171,16 +171,13 @@ void partial_bf16_kernel(PartialArgs a) {
     if (r0 >= sq.sq) return;
     const int mask = a.seqs.mask;
 
-    // The block's key range for this split, from its last row.
-    const int last_row = min(r0 + kBM, sq.sq) - 1;
-    const int64_t rl = row_last(sq, mask, last_row);
-    const int64_t kps = keys_per_split(rl, a.seqs.n_per_block, sq.splits);
-    // Split s covers [s*kps, (s+1)*kps) of the keys 0..rowLast.  Keys past
-    // lastValid are never visible, so an empty key range (lastValid = -1)
-    // gives an empty loop and no key is loaded.
-    const int64_t kend = min(rl + 1, sq.lv + 1);
-    int ks = (int)min((int64_t)it.split * kps, kend);
-    int ke = (int)min((int64_t)(it.split + 1) * kps, kend);
+    // The block's key range for this split, from its last row.  A split
+    // with no key for the whole block exits without writing anything: its
+    // slots are never read (the combine merges only the block's populated
+    // splits).
+    int ks, ke;
+    block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kBM, sq.sq) - 1, it.split, ks, ke);
+    if (ks >= ke) return;
     if (piece >= 0) {
         // piece p of P takes key tiles [nt p / P, nt (p + 1) / P) of the split
         const int nt = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
@@ -598,6 +595,9 @@ __global__ __launch_bounds__(kThreads) void merge_pieces_kernel(PartialArgs a) {
     if (it.split >= sq.splits) return;
     const int r0 = it.tile * kBM;
     if (r0 + r >= sq.sq) return;
+    int ks, ke;  // a block-empty split: no piece ran, nothing is written
+    block_split_range(sq, a.seqs.mask, a.seqs.n_per_block, min(r0 + kBM, sq.sq) - 1, it.split, ks, ke);
+    if (ks >= ke) return;
     const int64_t prow = sq.row0 + r0 + r;
     if (prow >= a.rows) return;
     const int P = a.pieces;

@@ -28,17 +28,12 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
     if (r0 >= sq.sq) return;
     const int mask = a.seqs.mask;
 
-    // Key range of this split for this block: the count formula at the
-    // block's last row decides keys per split.
-    const int last_row = min(r0 + kF32Rows, sq.sq) - 1;
-    const int64_t rl = row_last(sq, mask, last_row);
-    const int64_t kps = keys_per_split(rl, a.seqs.n_per_block, sq.splits);
-    // Split s covers [s*kps, (s+1)*kps) of the keys 0..rowLast.  Keys past
-    // lastValid are never visible, so an empty key range (lastValid = -1)
-    // gives an empty loop and no key is loaded.
-    const int64_t kend = min(rl + 1, sq.lv + 1);
-    const int ks = (int)min((int64_t)it.split * kps, kend);
-    const int ke = (int)min((int64_t)(it.split + 1) * kps, kend);
+    // Key range of this split for this block (the count formula at the
+    // block's last row).  A split with no key for the whole block exits
+    // without writing: the combine merges only the block's populated splits.
+    int ks, ke;
+    block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kF32Rows, sq.sq) - 1, it.split, ks, ke);
+    if (ks >= ke) return;
 
     const int lane = threadIdx.x;
     const int qrow = r0 + lane;

@@ -92,6 +92,32 @@ __device__ __forceinline__ int32_t valid_split_count(const Seq& s, int mask, int
 // Most key pieces one tail item of the partial kernel is split into.
 constexpr int kMaxPieces = 16;
 
+// Key range [ks, ke) of split `split` for the query block whose last row is
+// last_row: the count formula at that row gives keys per split, split s
+// covers [s*kps, (s+1)*kps) of the keys 0..rowLast, and keys past lastValid
+// are never visible (rocmlirTriton page, "Per-row valid-split counts", the
+// paragraph on conservative counts).  ks >= ke: the split is empty for the
+// whole block.
+__device__ __forceinline__ void block_split_range(const Seq& sq, int mask, int n_per_block, int last_row, int split,
+                                                  int& ks, int& ke) {
+    const int64_t rl = row_last(sq, mask, last_row);
+    const int64_t kps = keys_per_split(rl, n_per_block, sq.splits);
+    const int64_t kend = min(rl + 1, sq.lv + 1);
+    ks = (int)min((int64_t)split * kps, kend);
+    ke = (int)min((int64_t)(split + 1) * kps, kend);
+}
+
+// Splits that hold a key for the query block (of m_per_block rows) that row
+// r belongs to: the only ones the partial kernel writes for that block.
+__device__ __forceinline__ int block_populated_splits(const Seq& sq, int mask, int n_per_block, int m_per_block,
+                                                      int r) {
+    const int last_row = min((r / m_per_block + 1) * m_per_block, sq.sq) - 1;
+    const int64_t rl = row_last(sq, mask, last_row);
+    const int64_t kps = keys_per_split(rl, n_per_block, sq.splits);
+    const int64_t kend = min(rl + 1, sq.lv + 1);
+    return kend > 0 ? (int)min(ceil_div64(kend, kps), (int64_t)sq.splits) : 0;
+}
+
 // Arguments of every partial-attention kernel.
 struct PartialArgs {
     const void* q;
@@ -203,6 +229,8 @@ struct CombineArgs {
     int32_t dv;
     int32_t batch;
     int32_t row_blocks;  // blocks per head (set by the launcher)
+    int32_t m_per_block; // query block of the partial kernel (0: unknown, no block clamp)
+    int32_t pad_;
 };
 
 // Launchers (one translation unit each).

@@ -359,6 +359,8 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
     a.dv = p->head_dim_v;
     a.batch = p->batch;
     a.row_blocks = 0;
+    a.m_per_block = pick_partial(*p).m_per_block;  // 0 when no partial kernel exists for p
+    a.pad_ = 0;
     return hip_status(sk::launch_combine(a, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
 }
 

@@ -14,6 +14,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle
 from oracle import adapter
 from split_kv_attention_amd import attention, workloads
 
@@ -44,7 +45,8 @@ def run_gpu(w, seed=0, out_dtype=None, counts_in_combine=True, inputs=None, pois
     attention.run(prob, inputs["q"], inputs["k"], inputs["v"], counts, o_part, lse_part, out, lse_out,
                   counts_in_combine=counts_in_combine)
     torch.cuda.synchronize()
-    return inputs, prob, dict(counts=counts, o_part=o_part, lse_part=lse_part, out=out, lse_out=lse_out)
+    return inputs, prob, dict(counts=counts, o_part=o_part, lse_part=lse_part, out=out, lse_out=lse_out,
+                              poisoned=poison)
 
 
 def sample_rows(sq: int, n: int, seed: int, tile: int) -> np.ndarray:
@@ -92,7 +94,16 @@ def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=
             idx = torch.as_tensor(prow, device=res["o_part"].device)
             gL = res["lse_part"][h][:S_b][:, idx].double().cpu().numpy()
             gO = res["o_part"][h][:S_b][:, idx].double().cpu().numpy()
-            rL, rO = e["L_s"], e["O_s"]
+            rL, rO = e["L_s"].copy(), e["O_s"].copy()
+            # splits past the block's populated ones are not written (early exit);
+            # in the oracle they are (0, -inf) for every row of the block
+            pop = np.array([oracle.block_populated_splits(specs[b], mpb, int(q)) for q in rows])
+            skipped = np.arange(S_b)[:, None] >= pop[None, :]
+            assert np.isneginf(rL[skipped]).all() and (rO[skipped] == 0).all(), f"{label} oracle b={b}"
+            if res.get("poisoned"):
+                assert np.isnan(gL[skipped]).all() and np.isnan(gO[skipped]).all(), \
+                    f"{label} a block-empty split was written b={b} h={h}"
+            gL[skipped], gO[skipped] = rL[skipped], rO[skipped]
             assert not np.isnan(gL).any() and not np.isnan(gO).any(), f"{label} unwritten partial slot b={b} h={h}"
             np.testing.assert_array_equal(np.isneginf(gL), np.isneginf(rL), err_msg=f"{label} -inf pattern b={b} h={h}")
             fin = np.isfinite(rL)

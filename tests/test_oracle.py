@@ -145,6 +145,46 @@ def test_block_partition_covers_every_visible_key_once():
                     assert vis[q] < len(covered)
 
 
+def test_block_populated_splits_hold_every_key_the_block_sees():
+    """Real early exit: the splits a block still writes (populated) include
+    every split holding a key that any row of the block sees, and every other
+    split is (0, -inf) for all the block's rows, so a merge over
+    s < min(count, populated) is the merge over s < count."""
+    rng = np.random.default_rng(11)
+    n = 0
+    for spec in _sweep_specs():
+        if spec.sq > 40 or spec.sk > 60:
+            continue
+        Q, K, V = _rand(rng, spec.sq, 4), _rand(rng, spec.sk, 4), _rand(rng, spec.sk, 3)
+        counts = oracle.valid_split_counts(spec)
+        for mpb in (1, 8, 16):
+            pop = np.array([oracle.block_populated_splits(spec, mpb, q) for q in range(spec.sq)])
+            for q in range(spec.sq):
+                assert oracle.kernel_nonempty_splits(spec, mpb, q) <= pop[q] <= spec.split_kv, (spec, mpb, q)
+            O_s, L_s = oracle.partials(Q, K, V, 0.5, spec, mpb)
+            for q in range(spec.sq):
+                assert np.isneginf(L_s[pop[q]:, q]).all() and (O_s[pop[q]:, q] == 0).all(), (spec, mpb, q)
+            O1, l1 = oracle.combine(O_s, L_s, counts)
+            O2, l2 = oracle.combine(O_s, L_s, np.minimum(counts, pop))
+            np.testing.assert_array_equal(O1, O2)
+            np.testing.assert_array_equal(l1, l2)
+            n += 1
+    assert n > 100
+
+
+def test_block_populated_splits_special_cases():
+    # every row sees every key: one partition, populated = count = ceil(Sk / kps)
+    spec = SeqSpec(40, 300, 4, 32, MASK_NONE)
+    kps = 32 * math.ceil(math.ceil(300 / 32) / 4)  # 96
+    assert all(oracle.block_populated_splits(spec, 16, q) == math.ceil(300 / kps) == 4 for q in range(40))
+    # no key at all (lastValid = -1 after clamping an empty K): nothing to write
+    assert oracle.block_populated_splits(SeqSpec(5, 0, 3, 16, MASK_NONE), 4, 2) == 0
+    # causal, first block of 16 rows (keys 0..15): key tile 4 gives kps = 4 and
+    # all 4 splits hold keys; key tile 16 gives kps = 16 and only split 0 does
+    assert oracle.block_populated_splits(SeqSpec(64, 64, 4, 4, MASK_CAUSAL), 16, 0) == 4
+    assert oracle.block_populated_splits(SeqSpec(64, 64, 4, 16, MASK_CAUSAL), 16, 3) == 1
+
+
 def test_noncausal_counts_are_per_sequence():
     """Non-causal configs keep one count per batch-head (every row equal)."""
     for spec in _sweep_specs():
