@@ -70,7 +70,9 @@ typedef enum sk_mask_mode {
 
 typedef enum sk_dtype {
     SK_F32 = 0,
-    SK_BF16 = 1
+    SK_BF16 = 1,
+    SK_F16 = 2  /* IEEE half: storage only; scores, softmax and the merge stay f32
+                   (rocmlirTriton page, "f32 merge for f16/bf16") */
 } sk_dtype;
 
 typedef struct sk_problem {

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libsplitkv.so")
 
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_HIP = 0, 1, 2, 3
 SK_MASK_NONE, SK_MASK_CAUSAL, SK_MASK_PREFIX_CAUSAL = 0, 1, 2
-SK_F32, SK_BF16 = 0, 1
+SK_F32, SK_BF16, SK_F16 = 0, 1, 2
 
 # Every function include/splitkv.h declares.
 EXPORTS = (

@@ -16,10 +16,10 @@ from dataclasses import dataclass, field
 import torch
 
 from . import _lib
-from ._lib import SK_BF16, SK_F32, SK_MASK_CAUSAL, SK_MASK_NONE, SK_MASK_PREFIX_CAUSAL, SkProblem
+from ._lib import SK_BF16, SK_F16, SK_F32, SK_MASK_CAUSAL, SK_MASK_NONE, SK_MASK_PREFIX_CAUSAL, SkProblem
 
 _MASKS = {"none": SK_MASK_NONE, "causal": SK_MASK_CAUSAL, "prefix_causal": SK_MASK_PREFIX_CAUSAL}
-_DTYPES = {torch.float32: SK_F32, torch.bfloat16: SK_BF16}
+_DTYPES = {torch.float32: SK_F32, torch.bfloat16: SK_BF16, torch.float16: SK_F16}
 
 
 @dataclass
@@ -82,7 +82,7 @@ def build_problem(
     `partial_scratch` (and tensors on a GPU) the problem carries the scratch
     buffer sk_attn_partial balances its last round of workgroups with."""
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
+        raise TypeError("q, k, v must share one dtype: float32, bfloat16 or float16")
     dev = q.device
     keep = []
     p = SkProblem()

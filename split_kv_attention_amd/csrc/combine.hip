@@ -26,6 +26,16 @@ __device__ __forceinline__ void store4(__bf16* p, float4 v) {
     *reinterpret_cast<bf16x4*>(p) = r;
 }
 
+__device__ __forceinline__ void store4(_Float16* p, float4 v) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 r;
+    r[0] = (_Float16)v.x;  // round to nearest even
+    r[1] = (_Float16)v.y;
+    r[2] = (_Float16)v.z;
+    r[3] = (_Float16)v.w;
+    *reinterpret_cast<f16x4*>(p) = r;
+}
+
 // Buffer loads from a base that is uniform over the block, with a 32-bit
 // per-lane byte offset and a range of `bytes` (reads beyond it return 0):
 // no 64-bit address per lane and split.
@@ -210,8 +220,9 @@ hipError_t launch_combine(CombineArgs a, int out_dtype, hipStream_t stream) {
     const bool packed = a.seqs.cu_q != nullptr;
     a.row_blocks = (int32_t)combine_row_blocks(a.batch, a.seqs.max_sq, a.dv, packed);
     const dim3 grid((unsigned)(a.row_blocks * a.heads), packed ? a.batch : 1);
-    return out_dtype == SK_BF16 ? launch_out<__bf16>(a, grid, threads, stream)
-                                : launch_out<float>(a, grid, threads, stream);
+    if (out_dtype == SK_BF16) return launch_out<__bf16>(a, grid, threads, stream);
+    if (out_dtype == SK_F16) return launch_out<_Float16>(a, grid, threads, stream);
+    return launch_out<float>(a, grid, threads, stream);
 }
 
 }  // namespace sk

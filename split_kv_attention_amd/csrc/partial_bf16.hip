@@ -1,4 +1,5 @@
-// Split-KV partial attention, bf16 storage, bf16 MFMA with f32 accumulation.
+// Split-KV partial attention, bf16 or f16 storage, 16-bit MFMA with f32
+// accumulation.
 //
 // Per (sequence, head, split, block of 128 query rows) the kernel computes the
 // partial output O_s and log-sum-exp L_s over the split's keys (rocmlirTriton
@@ -40,8 +41,33 @@ namespace sk {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16-bit storage types: the operand vectors, the 32x32x16 MFMA and the
+// paired dot product used for row sums.  f16 and bf16 operands have the
+// same register layout, so the kernel is one template over them.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
+};
+template <>
+struct Elem<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
 
 constexpr int kBM = 128;    // query rows per workgroup
 constexpr int kBN = 64;     // keys per tile
@@ -148,10 +174,13 @@ __device__ __forceinline__ void tr_wait(s16x4 (&x)[8]) {
 // and LSE = m' + log(sum p) are unchanged; weights stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int DQK, int DV>
+template <typename T, int DQK, int DV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void partial_bf16_kernel(PartialArgs a) {
     using C = Cfg<DQK, DV>;
+    using E = Elem<T>;
+    using bf16x8 = typename E::v8;  // operand vector of the storage type
+    using bf16x2 = typename E::v2;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF_ELEMS];
 
     // Workgroups past n_main run piece `piece` of tail item n_main + tail_i.
@@ -321,13 +350,13 @@ void partial_bf16_kernel(PartialArgs a) {
         };
         auto mm = [&](i32x4_t(&x)[2], auto t_c) {
             constexpr int t = decltype(t_c)::value;
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]), qf[t], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[1]), qf[t], sacc[1], 0, 0, 0);
+            sacc[0] = E::mfma(__builtin_bit_cast(bf16x8, x[0]), qf[t], sacc[0]);
+            sacc[1] = E::mfma(__builtin_bit_cast(bf16x8, x[1]), qf[t], sacc[1]);
         };
         rd(f[0], std::integral_constant<int, 0>{});
-        [&]<int... T>(std::integer_sequence<int, T...>) {
+        [&]<int... Step>(std::integer_sequence<int, Step...>) {
             (([&] {
-                constexpr int t = T;
+                constexpr int t = Step;
                 if constexpr (t + 1 < DQK / 16) {
                     rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
                     k_wait<2>(f[t & 1][0], f[t & 1][1]);
@@ -406,9 +435,8 @@ void partial_bf16_kernel(PartialArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                pf[kb][j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+                pf[kb][j >> 3][j & 7] = (T)__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], cl2, -mc));
+        const bf16x2 ones = {(T)1.0f, (T)1.0f};
         rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -416,7 +444,7 @@ void partial_bf16_kernel(PartialArgs a) {
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int j = 0; j < 8; j += 2)
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, rs, false);
+                    rs = E::dot2(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, rs);
     };
     // The same, a slice of 2E elements at a time (E pairs), to be spread
     // over the steps of the next tile's GEMM0.
@@ -424,8 +452,7 @@ void partial_bf16_kernel(PartialArgs a) {
     constexpr int kPairsPerStep = (16 + kSteps - 1) / kSteps;
     auto weights_slice = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float mc_in, float& rs, auto step_c) {
         constexpr int step = decltype(step_c)::value;
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const bf16x2 ones = {(T)1.0f, (T)1.0f};
         if constexpr (step * kPairsPerStep < 16) {
             const float mc = mc_in;
 #pragma unroll
@@ -437,14 +464,14 @@ void partial_bf16_kernel(PartialArgs a) {
                     float x0 = fmaf(sacc[kb][j], cl2, -mc), x1 = fmaf(sacc[kb][j + 1], cl2, -mc);
                     asm volatile("" : "+v"(x0), "+v"(x1));  // keeps this slice below the step's wait
                     bf16x2 p2;
-                    p2[0] = (__bf16)__builtin_amdgcn_exp2f(x0);
-                    p2[1] = (__bf16)__builtin_amdgcn_exp2f(x1);
+                    p2[0] = (T)__builtin_amdgcn_exp2f(x0);
+                    p2[1] = (T)__builtin_amdgcn_exp2f(x1);
                     uint32_t packed = __builtin_bit_cast(uint32_t, p2);
                     asm volatile("" : "+v"(packed));  // keeps it above the next step's reads
                     p2 = __builtin_bit_cast(bf16x2, packed);
                     pf[kb][j >> 3][j & 7] = p2[0];
                     pf[kb][j >> 3][(j & 7) + 1] = p2[1];
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, rs, false);
+                    rs = E::dot2(p2, ones, rs);
                 }
             }
         }
@@ -483,7 +510,7 @@ void partial_bf16_kernel(PartialArgs a) {
 #pragma unroll
             for (int c = 0; c < DV / 32; ++c) {
                 const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * c], x[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-                o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[c], 0, 0, 0);
+                o[c] = E::mfma(va, p, o[c]);
             }
         };
         using I0 = std::integral_constant<int, 0>;
@@ -635,11 +662,11 @@ __global__ __launch_bounds__(kThreads) void merge_pieces_kernel(PartialArgs a) {
     if (part == 0) a.lse_part[slot] = den > 0.f ? m + logf(den) : -INFINITY;
 }
 
-template <int DQK, int DV>
+template <typename T, int DQK, int DV>
 hipError_t launch(const PartialArgs& a, hipStream_t stream) {
     const uint32_t n_tail = a.n_work - a.n_main;
     const uint32_t grid = a.n_main + n_tail * (uint32_t)a.pieces;
-    hipLaunchKernelGGL((partial_bf16_kernel<DQK, DV>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_bf16_kernel<T, DQK, DV>), dim3(grid), dim3(kThreads), 0, stream, a);
     if (n_tail > 0) {
         constexpr int kBlocks = kBM / (kThreads / (DV / 4));
         hipLaunchKernelGGL((merge_pieces_kernel<DV>), dim3(n_tail * kBlocks), dim3(kThreads), 0, stream, a);
@@ -648,12 +675,12 @@ hipError_t launch(const PartialArgs& a, hipStream_t stream) {
 }
 
 // Resident workgroups per CU (the same on every gfx950 device; cached).
-template <int DQK, int DV>
+template <typename T, int DQK, int DV>
 int blocks_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n > 0) return n;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<DQK, DV>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<T, DQK, DV>, kThreads, 0) != hipSuccess)
         return 0;
     cached.store(n, std::memory_order_relaxed);
     return n;
@@ -661,11 +688,15 @@ int blocks_per_cu() {
 
 }  // namespace
 
-PartialKernel find_partial_bf16(int d_qk, int d_v) {
-    if (d_qk == 64 && d_v == 64) return {launch<64, 64>, kBM, blocks_per_cu<64, 64>};
-    if (d_qk == 128 && d_v == 128) return {launch<128, 128>, kBM, blocks_per_cu<128, 128>};
-    if (d_qk == 192 && d_v == 128) return {launch<192, 128>, kBM, blocks_per_cu<192, 128>};
+template <typename T>
+PartialKernel find_partial_16(int d_qk, int d_v) {
+    if (d_qk == 64 && d_v == 64) return {launch<T, 64, 64>, kBM, blocks_per_cu<T, 64, 64>};
+    if (d_qk == 128 && d_v == 128) return {launch<T, 128, 128>, kBM, blocks_per_cu<T, 128, 128>};
+    if (d_qk == 192 && d_v == 128) return {launch<T, 192, 128>, kBM, blocks_per_cu<T, 192, 128>};
     return {nullptr, 0, nullptr};
 }
+
+PartialKernel find_partial_bf16(int d_qk, int d_v) { return find_partial_16<__bf16>(d_qk, d_v); }
+PartialKernel find_partial_f16(int d_qk, int d_v) { return find_partial_16<_Float16>(d_qk, d_v); }
 
 }  // namespace sk

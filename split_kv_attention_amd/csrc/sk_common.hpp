@@ -249,6 +249,7 @@ struct PartialKernel {
 };
 // Kernel for (dtype, d_qk, d_v), or {nullptr, 0} when not built.
 PartialKernel find_partial_bf16(int d_qk, int d_v);
+PartialKernel find_partial_f16(int d_qk, int d_v);
 PartialKernel find_partial_f32(int d_qk, int d_v);
 
 }  // namespace sk

@@ -41,7 +41,11 @@ int64_t rows_of(const sk_problem& p) {
     return p.cu_seqlens_q ? (int64_t)p.total_q : (int64_t)p.batch * p.max_seqlen_q;
 }
 
-int elem_bytes(int dtype) { return dtype == SK_BF16 ? 2 : 4; }
+int elem_bytes(int dtype) { return dtype == SK_F32 ? 4 : 2; }
+
+bool known_dtype(int dtype) { return dtype == SK_F32 || dtype == SK_BF16 || dtype == SK_F16; }
+
+const char* dtype_name(int dtype) { return dtype == SK_BF16 ? "bf16" : dtype == SK_F16 ? "f16" : "f32"; }
 
 // Checks every scalar field.  Pointer checks depend on the entry point.
 sk_status check_problem(const sk_problem* p) {
@@ -64,8 +68,8 @@ sk_status check_problem(const sk_problem* p) {
     if (p->n_per_block < 1) return fail(SK_ERR_INVALID_ARG, "n_per_block must be >= 1 (got %d)", p->n_per_block);
     if (p->mask != SK_MASK_NONE && p->mask != SK_MASK_CAUSAL && p->mask != SK_MASK_PREFIX_CAUSAL)
         return fail(SK_ERR_INVALID_ARG, "unknown mask mode %d", p->mask);
-    if (p->dtype != SK_F32 && p->dtype != SK_BF16) return fail(SK_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-    if (p->out_dtype != SK_F32 && p->out_dtype != SK_BF16)
+    if (!known_dtype(p->dtype)) return fail(SK_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (!known_dtype(p->out_dtype))
         return fail(SK_ERR_INVALID_ARG, "unknown out_dtype %d", p->out_dtype);
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
         return fail(SK_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
@@ -102,8 +106,9 @@ sk::SeqTable seq_table(const sk_problem& p) {
 bool aligned(const void* ptr, size_t bytes) { return ((uintptr_t)ptr % bytes) == 0; }
 
 sk::PartialKernel pick_partial(const sk_problem& p) {
-    return p.dtype == SK_BF16 ? sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v)
-                              : sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
+    if (p.dtype == SK_BF16) return sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v);
+    if (p.dtype == SK_F16) return sk::find_partial_f16(p.head_dim_qk, p.head_dim_v);
+    return sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
 }
 
 // Compute units of the current device (0 if unknown), cached per device.
@@ -164,7 +169,7 @@ int32_t auto_split_kv(const sk_problem& p) {
     sk_problem q = p;
     q.split_kv = 1;
     const sk::PartialKernel k = pick_partial(q);
-    if (!k.launch || p.dtype != SK_BF16) return 1;
+    if (!k.launch || p.dtype == SK_F32) return 1;
     const int64_t slots = partial_slots(k);
     const int64_t mpb = k.m_per_block;
     int64_t tiles = (int64_t)p.batch * ((p.max_seqlen_q + mpb - 1) / mpb);
@@ -268,7 +273,7 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
     const sk::PartialKernel kern = pick_partial(*p);
     if (!kern.launch)
         return fail(SK_ERR_UNSUPPORTED, "no partial kernel for dtype %s with head dims (%d, %d)",
-                    p->dtype == SK_BF16 ? "bf16" : "f32", p->head_dim_qk, p->head_dim_v);
+                    dtype_name(p->dtype), p->head_dim_qk, p->head_dim_v);
     const int64_t rows = rows_of(*p);
     if (p->batch == 0 || p->max_seqlen_q == 0 || rows == 0) return ok();
     if (!q || !k || !v || !o_part || !lse_part) return fail(SK_ERR_INVALID_ARG, "a tensor pointer is NULL");

@@ -6,8 +6,8 @@ packed-varlen prefill of the aiter page "[ASM][HIP][JIT][gfx942] Optimize
 long-context FMHA with split-KV" (H = 12, D_qk = 192, D_v = 128, Sq = 4096,
 Sk from 8K to 128K; Motivation and Test Result), which synthetic N(0, 1)
 tensors stand in for.  Q, K and V are drawn as float32 N(0, 1) from a torch
-generator seeded per (seed, tensor), then rounded to bf16 (round to nearest
-even) for bf16 workloads.  Both the HIP path and the oracle read the same
+generator seeded per (seed, tensor), then rounded to bf16 or f16 (round to
+nearest even) for 16-bit workloads.  Both the HIP path and the oracle read the same
 generated tensors.
 """
 from __future__ import annotations
@@ -49,7 +49,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[self.dtype]
 
 
 TINY_F32 = Workload(

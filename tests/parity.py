@@ -64,10 +64,14 @@ def _out_rows(w, out, b, h, rows, row0):
     return out[b, h][torch.as_tensor(rows, device=out.device)]
 
 
-def _bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+def _half_ulp(x: np.ndarray, mantissa_bits: int) -> np.ndarray:
+    """Half a unit in the last place of x in a format with that many stored
+    mantissa bits (bf16: 7, f16: 10; f16 subnormals below 2^-14)."""
     ax = np.abs(x)
     e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    return np.where(ax > 0, np.exp2(e - 8), 0.0)  # half of 2^(e-7)
+    if mantissa_bits == 10:
+        e = np.maximum(e, -14.0)
+    return np.where(ax > 0, np.exp2(e - mantissa_bits - 1), 0.0)
 
 
 def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=True, label=""):
@@ -79,7 +83,7 @@ def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=
     starts = adapter.row_starts(w)
     specs = adapter.seq_specs(w)
     gc = res["counts"].cpu().numpy()
-    out_bf16 = res["out"].dtype == torch.bfloat16
+    out_bits = {torch.bfloat16: 7, torch.float16: 10}.get(res["out"].dtype)
     num = den_g = den_r = 0.0
     stats = dict(max_err_out=0.0, max_err_lse=0.0, max_err_part=0.0, max_err_out_vs_rounded=0.0)
     for (b, h), e in exp.items():
@@ -117,9 +121,9 @@ def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=
         r = e["O"]
         assert np.isfinite(g).all(), f"{label} non-finite output b={b} h={h}"
         err = np.abs(g - r)
-        if out_bf16:
-            allow = tol + _bf16_half_ulp(r)
-            rr = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
+        if out_bits:
+            allow = tol + _half_ulp(r, out_bits)
+            rr = torch.from_numpy(r).to(res["out"].dtype).double().numpy()
             stats["max_err_out_vs_rounded"] = max(stats["max_err_out_vs_rounded"], float(np.abs(g - rr).max()))
         else:
             allow = tol

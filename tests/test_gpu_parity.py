@@ -219,6 +219,43 @@ def test_automatic_split_end_to_end():
     log(f"  S={S} {st}")
 
 
+# f16 storage (scores, softmax and merge in f32; rocmlirTriton page, "f32
+# merge for f16/bf16"): the same kernels on IEEE half operands
+SMALL_F16 = [
+    _shrink(workloads.LONG_PREFILL, name="f16_prefill_Sq300_Sk2000_S3", sq=(300,), sk=(2000,), dtype="f16"),
+    _shrink(workloads.CAUSAL_BF16, name="f16_causal_d64", d_qk=64, d_v=64, sq=(200, 200), sk=(333, 333),
+            dtype="f16"),
+    _shrink(workloads.VARLEN_BATCH_PREFIX, name="f16_varlen_prefix", sq=(130, 1, 257, 64), sk=(500, 70, 1500, 3000),
+            split_kv_per_seq=(2, 4, 6, 8), prefix_offset_per_seq=(370, 69, 1243, 2936),
+            last_valid_per_seq=(499, 69, 1499, 2999), dtype="f16"),
+    _shrink(workloads.DECODE_BF16, name="f16_decode_B4_H4_Sk3000", sq=(1,) * 4, sk=(3000,) * 4, heads=4, dtype="f16"),
+    _shrink(workloads.LONG_PREFILL, name="f16_tail_split_H2_Sq256_Sk8192_S2", heads=2, sq=(256,), sk=(8192,),
+            split_kv=2, dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_F16, ids=lambda w: w.name)
+def test_f16_storage_all_rows(w):
+    log(f"f16 {w.name}")
+    inputs, prob, res = run_gpu(w, seed=9)
+    assert res["out"].dtype == torch.float16
+    st = compare(w, inputs, prob, res, label=w.name)
+    log(f"  {st}")
+    # f32 output from f16 inputs: one rounding less
+    inputs, prob, res = run_gpu(w, seed=9, out_dtype=torch.float32)
+    compare(w, inputs, prob, res, label=w.name + "/f32out")
+
+
+def test_f16_scores_far_above_the_reference():
+    """Weights against a stale reference can exceed the f16 range; the range
+    check then takes the max update and recomputes them."""
+    w = _shrink(workloads.LONG_PREFILL, name="f16_growing_scores", sq=(150,), sk=(3000,), split_kv=2, dtype="f16")
+    inputs = workloads.make_inputs(w, DEV, 12)
+    inputs["k"][200:] *= 6  # later keys score up to ~6x higher than the first tile's
+    inputs, prob, res = run_gpu(w, inputs=inputs)
+    compare(w, inputs, prob, res, label=w.name)
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_small_cases_all_rows(w):
     log(f"e2e {w.name}")
