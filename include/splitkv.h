@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SK_ABI_VERSION 2
+#define SK_ABI_VERSION 3
 
 typedef enum sk_status {
     SK_OK = 0,
@@ -120,6 +120,13 @@ typedef struct sk_problem {
      * time.  NULL (or too small) runs every item whole. */
     void* partial_scratch;
     int64_t partial_scratch_bytes;
+    /* Sliding window (>= 0) or -1 for none.  The aiter page's split path
+     * takes the caller's window without defining it; here a row q sees only
+     * keys k >= q + off - window_left, with off = prefix_offset(_per_seq)
+     * under PREFIX_CAUSAL and 0 otherwise (the position the causal rule
+     * uses), on top of every other rule.  Counts do not change: the count
+     * formula depends only on the last visible key. */
+    int64_t window_left;
 } sk_problem;
 
 /* ABI version of the library (SK_ABI_VERSION of the header it was built from). */

@@ -30,6 +30,7 @@ def seq_specs(w) -> list:
                 mask=_MASKS[w.mask],
                 prefix_offset=w.prefix_offset_per_seq[b] if w.prefix_offset_per_seq else w.prefix_offset,
                 last_valid=w.last_valid_per_seq[b] if w.last_valid_per_seq else w.last_valid_kv_index,
+                window_left=getattr(w, "window_left", -1),
             )
         )
     return specs

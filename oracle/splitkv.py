@@ -23,6 +23,7 @@ next to the code that takes it.
 Functions
 ---------
 visible_last_key   last key a query row may see (vis(q)); < 0 means none
+visible_first_key  first key a query row may see (0 without a sliding window)
 valid_split_counts per-row valid-split counts [R, Per-row valid-split counts]
 block_split_ranges the key range of every split for one M block
                    [R, Per-row valid-split counts, the block's last row]
@@ -60,6 +61,13 @@ class SeqSpec:
     last_valid    last_valid_kv_index; < 0 selects the default sk - 1 [R].
                   Reading: a value beyond the sequence is clamped to sk - 1,
                   because keys past the end do not exist.
+    window_left   sliding window: [A, Technical Details] lets the split path
+                  take the caller's window without defining it.  Reading: a
+                  left window of that many keys behind the row's position
+                  q + offset (the position the causal rule uses; offset 0
+                  without a prefix), i.e. keys k >= q + offset - window_left;
+                  < 0 means no window.  The count formula is unchanged: it
+                  depends only on the last visible key.
     """
 
     sq: int
@@ -69,6 +77,7 @@ class SeqSpec:
     mask: int = MASK_NONE
     prefix_offset: int = 0
     last_valid: int = -1
+    window_left: int = -1
 
     def __post_init__(self):
         if self.sq < 0 or self.sk < 0:
@@ -111,6 +120,25 @@ def visible_last_key(rows, spec: SeqSpec) -> np.ndarray:
     if spec.mask == MASK_NONE:
         return np.full(rows.shape, lv, dtype=np.int64)
     return np.minimum(rows + spec.offset, lv)
+
+
+def visible_first_key(rows, spec: SeqSpec) -> np.ndarray:
+    """The first key index row q may attend to: q + offset - window_left with a
+    window (see SeqSpec), else 0.  Keys below 0 do not exist, so values <= 0
+    all mean "from the first key"."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if spec.window_left < 0:
+        return np.zeros(rows.shape, dtype=np.int64)
+    return np.maximum(rows + spec.offset - spec.window_left, 0)
+
+
+def visible_keys(rows, spec: SeqSpec, keys) -> np.ndarray:
+    """Boolean [rows, keys]: key k is visible to row q iff
+    visible_first_key(q) <= k <= visible_last_key(q)."""
+    keys = np.asarray(keys, dtype=np.int64)
+    lo = visible_first_key(rows, spec)
+    hi = visible_last_key(rows, spec)
+    return (keys[None, :] >= lo[:, None]) & (keys[None, :] <= hi[:, None])
 
 
 def row_last(rows, spec: SeqSpec) -> np.ndarray:
@@ -196,9 +224,7 @@ def unsplit(Q, K, V, scale, spec: SeqSpec, rows=None):
     [R, Summary and NaN-safe merge: the merged output equals attention].
     """
     rows = np.arange(spec.sq) if rows is None else np.asarray(rows)
-    vis = visible_last_key(rows, spec)
-    keys = np.arange(spec.sk)
-    visible = keys[None, :] <= vis[:, None]
+    visible = visible_keys(rows, spec, np.arange(spec.sk))
     return _softmax_attention(Q, K[: spec.sk], V[: spec.sk], scale, visible)
 
 
@@ -217,15 +243,13 @@ def partials(Q, K, V, scale, spec: SeqSpec, m_per_block: int, rows=None):
     dv = V.shape[1]
     O = np.zeros((S, len(rows), dv))
     L = np.full((S, len(rows)), -np.inf)
-    vis = visible_last_key(rows, spec)
     blocks = rows // m_per_block
     for j in np.unique(blocks):
         sel = np.nonzero(blocks == j)[0]
         for s, (a, b) in enumerate(block_split_ranges(spec, m_per_block, int(j))):
             if b <= a:
                 continue
-            keys = np.arange(a, b)
-            visible = keys[None, :] <= vis[sel, None]
+            visible = visible_keys(rows[sel], spec, np.arange(a, b))
             o, l = _softmax_attention(Q[sel], K[a:b], V[a:b], scale, visible)
             O[s, sel] = o
             L[s, sel] = l
@@ -268,16 +292,19 @@ def split_attention(Q, K, V, scale, spec: SeqSpec, m_per_block: int, rows=None):
 
 def visible_pairs(spec: SeqSpec) -> int:
     """Number of visible (query, key) pairs of one head: the algorithmic work unit."""
-    vis = visible_last_key(np.arange(spec.sq), spec)
-    return int(np.clip(vis + 1, 0, None).sum())
+    rows = np.arange(spec.sq)
+    vis = visible_last_key(rows, spec)
+    first = visible_first_key(rows, spec)
+    return int(np.clip(vis + 1 - first, 0, None).sum())
 
 
 def kernel_nonempty_splits(spec: SeqSpec, m_per_block: int, row: int) -> int:
     """Number of splits of `row`'s block whose range holds a key the row sees."""
     vis = int(visible_last_key([row], spec)[0])
+    first = int(visible_first_key([row], spec)[0])
     n = 0
     for a, b in block_split_ranges(spec, m_per_block, row // m_per_block):
-        if b > a and a <= vis:
+        if b > a and a <= vis and b - 1 >= first:
             n += 1
     return n
 
@@ -305,6 +332,8 @@ __all__ = [
     "LOWEST_FINITE",
     "SeqSpec",
     "visible_last_key",
+    "visible_first_key",
+    "visible_keys",
     "row_last",
     "keys_per_split",
     "valid_split_counts",

@@ -72,6 +72,7 @@ class SkProblem(ctypes.Structure):
         ("o_stride_batch", ctypes.c_int64),
         ("partial_scratch", ctypes.c_void_p),
         ("partial_scratch_bytes", ctypes.c_int64),
+        ("window_left", ctypes.c_int64),
     ]
 
 

@@ -77,6 +77,7 @@ def build_problem(
     out_dtype: torch.dtype | None = None,
     out_strides: tuple[int, int, int] | None = None,
     partial_scratch: bool = True,
+    window_left: int = -1,
 ) -> Problem:
     """Describe one forward call; tensors stay where they are.  With
     `partial_scratch` (and tensors on a GPU) the problem carries the scratch
@@ -139,6 +140,7 @@ def build_problem(
     p.last_valid_kv_index = last_valid_kv_index
     p.softmax_scale = softmax_scale if softmax_scale is not None else d_qk ** -0.5
     p.reserved0 = 0
+    p.window_left = window_left
     for name, val in (
         ("cu_seqlens_q", cu_seqlens_q),
         ("cu_seqlens_k", cu_seqlens_k),

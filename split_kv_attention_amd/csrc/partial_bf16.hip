@@ -214,9 +214,16 @@ void partial_bf16_kernel(PartialArgs a) {
         ke = min(ks + hi * kBN, ke);
         ks = min(ks + lo * kBN, ke);
     }
+    // Sliding window: whole tiles below the first row's first visible key
+    // (the smallest in the block) hold no key any row sees; start past them.
+    const int64_t win = a.seqs.window_left;
+    {
+        const int64_t lo_first = vis_first(sq, win, r0);
+        if (lo_first > ks) ks = (int)min((int64_t)ke, ks + (lo_first - ks) / kBN * kBN);
+    }
     // Smallest visibility limit in the block (its first row): tiles entirely
     // below it and inside the split need no per-element mask.
-    const int64_t vis_first = vis_last(sq, mask, r0);
+    const int64_t vis_top = vis_last(sq, mask, r0);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases in SGPRs
@@ -226,8 +233,9 @@ void partial_bf16_kernel(PartialArgs a) {
     const int qrow = r0 + wave * 32 + col;
     const bool row_ok = qrow < sq.sq;
     const bool wave_active = (r0 + wave * 32) < sq.sq;
-    // Visibility limit of this lane's row, clamped into int range (keys are int).
+    // Visibility limits of this lane's row, clamped into int range (keys are int).
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
+    const int lo_q = (int)min(vis_first(sq, win, qrow), (int64_t)0x7fffffff);
 
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) +
                             (sq.krow0 >= 0 ? sq.krow0 * a.k_row : (int64_t)it.batch * a.k_batch) +
@@ -325,9 +333,12 @@ void partial_bf16_kernel(PartialArgs a) {
     const int v_q = 2 * g2 + ((s16 & 3) >> 1);
     const int v_in = (s16 & 1) * 4;
 
-    // Tiles [ks, full_end) lie inside the split and below every row's limit.
-    const int64_t full_last = min((int64_t)ke - kBN, vis_first - (kBN - 1));  // last unmasked tile start
+    // Tiles [full_start, full_end) lie inside the split, below every row's
+    // last visible key and (with a window) at or above every row's first.
+    const int64_t full_last = min((int64_t)ke - kBN, vis_top - (kBN - 1));  // last unmasked tile start
     const int full_end = full_last < ks ? ks : (int)(ks + ((full_last - ks) / kBN + 1) * kBN);
+    const int64_t lo_last = vis_first(sq, win, min(r0 + kBM, sq.sq) - 1);  // the block's largest first key
+    const int full_start = lo_last <= ks ? ks : (int)min((int64_t)ke, ks + ceil_div64(lo_last - ks, kBN) * kBN);
 
     // GEMM0: S^T[key][query] for the two 32-key blocks of tile Kb; K
     // fragments for step t + 1 are read while step t multiplies.
@@ -375,11 +386,14 @@ void partial_bf16_kernel(PartialArgs a) {
     // holds key kt + 32*kb + 8*(j/4) + 4*half + (j%4) for query column `col`.
     auto mask_tile = [&](int kt, f32x16(&sacc)[2]) {
         const int lim = min(ke - 1, vis_q) - kt - half * 4;  // last visible key, relative
+        const int first = lo_q - kt - half * 4;               // first visible key, relative
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (kb * 32 + (j >> 2) * 8 + (j & 3) > lim) sacc[kb][j] = -INFINITY;
+            for (int j = 0; j < 16; ++j) {
+                const int rel = kb * 32 + (j >> 2) * 8 + (j & 3);
+                if (rel > lim || rel < first) sacc[kb][j] = -INFINITY;
+            }
     };
     // Reference-max update from a tile's complete scores.  The reference max
     // moves only when it grew by more than the threshold for some row of the
@@ -414,12 +428,13 @@ void partial_bf16_kernel(PartialArgs a) {
     // and the output accumulator stay far inside f32 / bf16 range, and the
     // result O = sum p V / sum p does not depend on the reference.
     auto prepare = [&](int kt, f32x16(&sacc)[2]) -> bool {
-        const bool masked = kt >= full_end;
+        const bool masked = kt >= full_end || kt < full_start;
         if (masked) {
             asm volatile("");  // a real branch: most tiles need no mask
             mask_tile(kt, sacc);
         }
-        if (masked || kt == ks) {
+        // the first unmasked tile too: rows may have seen nothing before it
+        if (masked || kt == ks || kt == full_start) {
             max_update(sacc);
             return true;
         }

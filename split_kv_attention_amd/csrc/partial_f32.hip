@@ -34,11 +34,19 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
     int ks, ke;
     block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kF32Rows, sq.sq) - 1, it.split, ks, ke);
     if (ks >= ke) return;
+    // Sliding window: tiles below the first row's first visible key hold
+    // nothing any row sees.
+    const int64_t win = a.seqs.window_left;
+    {
+        const int64_t lo_first = vis_first(sq, win, r0);
+        if (lo_first > ks) ks = (int)min((int64_t)ke, ks + (lo_first - ks) / BN * BN);
+    }
 
     const int lane = threadIdx.x;
     const int qrow = r0 + lane;
     const bool row_ok = qrow < sq.sq;
     const int64_t vis = vis_last(sq, mask, qrow);
+    const int64_t lo = vis_first(sq, win, qrow);
 
     const float* qp = reinterpret_cast<const float*>(a.q) +
                       (a.seqs.cu_q ? (sq.row0 + qrow) * a.q_row : (int64_t)it.batch * a.q_batch + (int64_t)qrow * a.q_row) +
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
                 dot = fmaf(qv[4 * d + 3], kk.w, dot);
             }
             const int key = kt + j;
-            sc[j] = (key < ke && key <= vis) ? dot : -INFINITY;
+            sc[j] = (key < ke && key <= vis && key >= lo) ? dot : -INFINITY;
             mx = fmaxf(mx, sc[j]);
         }
         // Online softmax in base 2; a row with nothing visible yet keeps

@@ -24,6 +24,7 @@ struct SeqTable {
     int32_t pad_;
     int64_t prefix_offset;
     int64_t last_valid_kv_index;
+    int64_t window_left;  // < 0: no sliding window
 };
 
 // One sequence, resolved.
@@ -70,6 +71,12 @@ __device__ __forceinline__ Seq load_seq(const SeqTable& t, int b) {
 // at the last valid key (rocmlirTriton page, "Per-row valid-split counts").
 __device__ __forceinline__ int64_t vis_last(const Seq& s, int mask, int64_t q) {
     return (mask == SK_MASK_NONE) ? s.lv : min(q + s.off, s.lv);
+}
+
+// First key index row q may see: q + off - window_left under a sliding
+// window (0 and below: from the first key), else 0.
+__device__ __forceinline__ int64_t vis_first(const Seq& s, int64_t window_left, int64_t q) {
+    return window_left < 0 ? 0 : max((int64_t)0, q + s.off - window_left);
 }
 
 // rowLast = clamp(q + prefix_offset, 0, lastValid), lower clamp last, so an

@@ -75,6 +75,7 @@ sk_status check_problem(const sk_problem* p) {
         return fail(SK_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
     if (p->reserved0 != 0) return fail(SK_ERR_INVALID_ARG, "reserved0 must be 0");
     if (p->partial_scratch_bytes < 0) return fail(SK_ERR_INVALID_ARG, "partial_scratch_bytes must be >= 0");
+    if (p->window_left < -1) return fail(SK_ERR_INVALID_ARG, "window_left must be >= 0, or -1 for none");
     const int64_t strides[] = {p->q_stride_row, p->q_stride_head, p->q_stride_batch, p->k_stride_row,
                                p->k_stride_head, p->k_stride_batch, p->v_stride_row, p->v_stride_head,
                                p->v_stride_batch, p->o_stride_row, p->o_stride_head, p->o_stride_batch};
@@ -100,6 +101,7 @@ sk::SeqTable seq_table(const sk_problem& p) {
     t.pad_ = 0;
     t.prefix_offset = p.prefix_offset;
     t.last_valid_kv_index = p.last_valid_kv_index;
+    t.window_left = p.window_left;
     return t;
 }
 

@@ -37,6 +37,7 @@ class Workload:
     last_valid_kv_index: int = -1
     last_valid_per_seq: tuple | None = None
     scale: float | None = None
+    window_left: int = -1  # sliding window (keys behind q + offset), -1 = none
     notes: str = field(default="", compare=False)
 
     @property
@@ -131,7 +132,7 @@ def problem_kwargs(w: Workload, inputs: dict) -> dict:
         split_kv=w.split_kv, n_per_block=w.n_per_block, mask=w.mask, prefix_offset=w.prefix_offset,
         last_valid_kv_index=w.last_valid_kv_index, softmax_scale=w.softmax_scale,
         split_kv_per_seq=w.split_kv_per_seq, prefix_offset_per_seq=w.prefix_offset_per_seq,
-        last_valid_per_seq=w.last_valid_per_seq,
+        last_valid_per_seq=w.last_valid_per_seq, window_left=w.window_left,
     )
     if w.packed:
         kw.update(cu_seqlens_q=inputs["cu_seqlens_q"], cu_seqlens_k=inputs["cu_seqlens_k"],

@@ -61,6 +61,7 @@ def _good():
     p.split_kv, p.n_per_block = 4, 64
     p.mask, p.dtype, p.out_dtype = sk.SK_MASK_CAUSAL, sk.SK_BF16, sk.SK_BF16
     p.last_valid_kv_index = -1
+    p.window_left = -1
     p.softmax_scale = 128 ** -0.5
     p.q_stride_row, p.q_stride_head, p.q_stride_batch = 128, 100 * 128, 4 * 100 * 128
     p.k_stride_row, p.k_stride_head, p.k_stride_batch = 128, 300 * 128, 4 * 300 * 128
@@ -113,6 +114,7 @@ BAD = [
     ("reserved0", 1, sk.SK_ERR_INVALID_ARG),
     ("k_stride_row", -8, sk.SK_ERR_INVALID_ARG),
     ("partial_scratch_bytes", -1, sk.SK_ERR_INVALID_ARG),
+    ("window_left", -2, sk.SK_ERR_INVALID_ARG),
 ]
 
 

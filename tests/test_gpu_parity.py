@@ -256,6 +256,36 @@ def test_f16_scores_far_above_the_reference():
     compare(w, inputs, prob, res, label=w.name)
 
 
+# Sliding window (reading: keys k >= q + off - window_left, on top of the
+# other rules; the count formula is unchanged).  Whole tiles below a block's
+# window are skipped, tiles the window cuts are masked per element.
+WINDOW = [
+    _shrink(workloads.CAUSAL_BF16, name="window_causal_100", sq=(300, 300), sk=(300, 300), split_kv=3,
+            window_left=100),
+    _shrink(workloads.CAUSAL_BF16, name="window_causal_0_diagonal_only", sq=(200, 200), sk=(200, 200), split_kv=2,
+            window_left=0),
+    _shrink(workloads.LONG_PREFILL, name="window_bottom_right_Sq300_Sk2000", sq=(300,), sk=(2000,),
+            mask="prefix_causal", prefix_offset=1700, window_left=500),
+    _shrink(workloads.LONG_PREFILL, name="window_no_mask_64", sq=(257,), sk=(900,), mask="none", window_left=64),
+    _shrink(workloads.VARLEN_BATCH_PREFIX, name="window_varlen_prefix", sq=(130, 1, 257, 64), sk=(500, 70, 1500, 3000),
+            split_kv_per_seq=(2, 4, 6, 8), prefix_offset_per_seq=(370, 69, 1243, 2936),
+            last_valid_per_seq=(499, 69, 1499, 2999), window_left=300),
+    _shrink(workloads.TINY_F32, name="window_f32_causal", mask="causal", sq=(100,), sk=(100,), split_kv=3,
+            window_left=20),
+    _shrink(workloads.CAUSAL_BF16, name="window_wider_than_all", sq=(200, 200), sk=(333, 333), window_left=100000),
+    _shrink(workloads.LONG_PREFILL, name="window_tail_split_H2_Sq256_Sk8192", heads=2, sq=(256,), sk=(8192,),
+            split_kv=2, mask="prefix_causal", prefix_offset=7936, window_left=1000),
+]
+
+
+@pytest.mark.parametrize("w", WINDOW, ids=lambda w: w.name)
+def test_sliding_window_all_rows(w):
+    log(f"window {w.name}")
+    inputs, prob, res = run_gpu(w, seed=13)
+    st = compare(w, inputs, prob, res, label=w.name)
+    log(f"  {st}")
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_small_cases_all_rows(w):
     log(f"e2e {w.name}")

@@ -145,6 +145,62 @@ def test_block_partition_covers_every_visible_key_once():
                     assert vis[q] < len(covered)
 
 
+def _brute_window_attention(Q, K, V, scale, q, lo, hi):
+    """Pure-Python softmax attention of row q over keys lo..hi (inclusive)."""
+    keys = [k for k in range(len(K)) if lo <= k <= hi]
+    if not keys:
+        return [0.0] * len(V[0]), -math.inf
+    x = [scale * sum(a * b for a, b in zip(Q[q], K[k])) for k in keys]
+    m = max(x)
+    e = [math.exp(v - m) for v in x]
+    z = sum(e)
+    return [sum(e[i] * V[k][d] for i, k in enumerate(keys)) / z for d in range(len(V[0]))], m + math.log(z)
+
+
+@pytest.mark.parametrize("mask,off,win,lv", [
+    (MASK_CAUSAL, 0, 3, -1), (MASK_CAUSAL, 0, 0, -1), (MASK_PREFIX_CAUSAL, 9, 5, -1),
+    (MASK_PREFIX_CAUSAL, -3, 4, 20), (MASK_NONE, 0, 6, -1), (MASK_PREFIX_CAUSAL, 2, 40, 12),
+])
+def test_sliding_window_matches_brute_force(mask, off, win, lv):
+    """Left window: row q sees keys q + off - win .. vis(q), checked against
+    explicit loops; split -> merge reproduces it for several split shapes."""
+    rng = np.random.default_rng(31)
+    sq, sk, d = 14, 26, 3
+    Q, K, V = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, 2)
+    spec = SeqSpec(sq, sk, 3, 4, mask, off, lv, window_left=win)
+    O, lse = oracle.unsplit(Q, K, V, 0.7, spec)
+    last = spec.last_valid_index
+    for q in range(sq):
+        hi = min(q + spec.offset, last) if mask != MASK_NONE else last
+        o, l = _brute_window_attention(Q.tolist(), K.tolist(), V.tolist(), 0.7, q, q + spec.offset - win, hi)
+        np.testing.assert_allclose(O[q], o, rtol=1e-12, atol=1e-12)
+        assert (lse[q] == l) if l == -math.inf else abs(lse[q] - l) < 1e-12
+    for S, nPB, mpb in ((1, 4, 4), (3, 4, 8), (5, 2, 16), (9, 1, 3)):
+        sp = SeqSpec(sq, sk, S, nPB, mask, off, lv, window_left=win)
+        O2, lse2, *_ = oracle.split_attention(Q, K, V, 0.7, sp, mpb)
+        np.testing.assert_allclose(O2, O, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(np.isneginf(lse2), np.isneginf(lse))
+
+
+def test_sliding_window_matches_torch_sdpa_with_explicit_mask():
+    rng = np.random.default_rng(32)
+    sq, sk, d = 40, 70, 16
+    Q, K, V = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, 8)
+    spec = SeqSpec(sq, sk, 4, 8, MASK_PREFIX_CAUSAL, 30, window_left=12)
+    O, _ = oracle.unsplit(Q, K, V, 0.25, spec)
+    q = np.arange(sq)[:, None]
+    k = np.arange(sk)[None, :]
+    allowed = torch.from_numpy((k <= q + 30) & (k >= q + 30 - 12))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None],
+        attn_mask=allowed[None, None], scale=0.25)[0, 0].numpy()
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-12)
+    # the window leaves the count formula alone: it is conservative still
+    assert np.array_equal(oracle.valid_split_counts(spec),
+                          oracle.valid_split_counts(SeqSpec(sq, sk, 4, 8, MASK_PREFIX_CAUSAL, 30)))
+    assert oracle.visible_pairs(spec) == sq * 13
+
+
 def test_block_populated_splits_hold_every_key_the_block_sees():
     """Real early exit: the splits a block still writes (populated) include
     every split holding a key that any row of the block sees, and every other
