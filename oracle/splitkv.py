@@ -228,6 +228,38 @@ def unsplit(Q, K, V, scale, spec: SeqSpec, rows=None):
     return _softmax_attention(Q, K[: spec.sk], V[: spec.sk], scale, visible)
 
 
+def unsplit_backward(Q, K, V, dO, scale, spec: SeqSpec):
+    """Gradients dQ [sq, Dqk], dK [sk, Dqk], dV [sk, Dv] of the plain softmax
+    attention of `unsplit` for the output gradient dO [sq, Dv] (f64).
+
+    [A] leaves backward coverage of split-KV long-K attention open; the
+    method's output is plain attention over the visible keys, so its gradient
+    is that of attention: with P = softmax(x) over the visible keys,
+        D_q = sum_v dO[q, v] O[q, v]
+        dP  = dO V^T,   dS = P * (dP - D_q)
+        dQ  = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
+    A row with no visible key has P = 0 and contributes nothing.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)[: spec.sk]
+    V = np.asarray(V, dtype=np.float64)[: spec.sk]
+    dO = np.asarray(dO, dtype=np.float64)
+    rows = np.arange(spec.sq)
+    visible = visible_keys(rows, spec, np.arange(spec.sk))
+    x = scale * (Q @ K.T)
+    x = np.where(visible, x, -np.inf)
+    has = visible.any(axis=1)
+    m = np.where(has, x.max(axis=1, initial=-np.inf), 0.0)
+    e = np.where(visible, np.exp(x - m[:, None]), 0.0)
+    z = e.sum(axis=1)
+    P = np.where(has[:, None], e / np.where(has, z, 1.0)[:, None], 0.0)
+    O = P @ V
+    D = (dO * O).sum(axis=1)
+    dP = dO @ V.T
+    dS = P * (dP - D[:, None])
+    return scale * (dS @ K), scale * (dS.T @ Q), P.T @ dO
+
+
 def partials(Q, K, V, scale, spec: SeqSpec, m_per_block: int, rows=None):
     """Per-split partial outputs O_s [S, rows, Dv] and LSE L_s [S, rows].
 
@@ -339,6 +371,7 @@ __all__ = [
     "valid_split_counts",
     "block_split_ranges",
     "unsplit",
+    "unsplit_backward",
     "partials",
     "combine",
     "split_attention",

@@ -201,6 +201,51 @@ def test_sliding_window_matches_torch_sdpa_with_explicit_mask():
     assert oracle.visible_pairs(spec) == sq * 13
 
 
+@pytest.mark.parametrize("mask,off,win,lv", [
+    (MASK_NONE, 0, -1, -1), (MASK_CAUSAL, 0, -1, -1), (MASK_PREFIX_CAUSAL, 6, -1, 15),
+    (MASK_PREFIX_CAUSAL, -4, -1, -1), (MASK_CAUSAL, 0, 3, -1),
+])
+def test_backward_matches_torch_autograd_f64(mask, off, win, lv):
+    """The gradient formulas against torch autograd through float64 SDPA with
+    the same explicit visibility mask (rows with no visible key are given a
+    zero gradient on both sides)."""
+    rng = np.random.default_rng(41)
+    sq, sk, d, dv = 13, 22, 6, 5
+    Q, K, V, dO = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, dv), _rand(rng, sq, dv)
+    spec = SeqSpec(sq, sk, 3, 4, mask, off, lv, window_left=win)
+    dQ, dK, dV = oracle.unsplit_backward(Q, K, V, dO, 0.6, spec)
+    vis = torch.from_numpy(osk.visible_keys(np.arange(sq), spec, np.arange(sk)))
+    has = vis.any(dim=1)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_() for a in (Q, K, V))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[has][None, None], tk[None, None], tv[None, None], attn_mask=vis[has][None, None], scale=0.6)[0, 0]
+    o.backward(torch.from_numpy(dO)[has])
+    np.testing.assert_allclose(dQ, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dK, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of <dO, unsplit(...)> in a few coordinates of Q, K and V."""
+    rng = np.random.default_rng(42)
+    sq, sk, d, dv = 5, 9, 3, 2
+    Q, K, V, dO = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, dv), _rand(rng, sq, dv)
+    spec = SeqSpec(sq, sk, 2, 4, MASK_PREFIX_CAUSAL, 2, window_left=4)
+    grads = oracle.unsplit_backward(Q, K, V, dO, 0.9, spec)
+
+    def f(Q, K, V):
+        return float((oracle.unsplit(Q, K, V, 0.9, spec)[0] * dO).sum())
+
+    h = 1e-6
+    for which, (i, j) in ((0, (1, 2)), (0, (4, 0)), (1, (3, 1)), (1, (6, 2)), (2, (2, 0)), (2, (5, 1))):
+        args = [Q.copy(), K.copy(), V.copy()]
+        args[which][i, j] += h
+        fp = f(*args)
+        args[which][i, j] -= 2 * h
+        fm = f(*args)
+        assert abs((fp - fm) / (2 * h) - grads[which][i, j]) < 1e-7
+
+
 def test_block_populated_splits_hold_every_key_the_block_sees():
     """Real early exit: the splits a block still writes (populated) include
     every split holding a key that any row of the block sees, and every other
