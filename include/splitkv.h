@@ -1,5 +1,6 @@
 /*
- * libsplitkv: split-KV attention forward for AMD Instinct MI355X (gfx950).
+ * libsplitkv: split-KV attention forward (and its backward) for AMD Instinct
+ * MI355X (gfx950).
  *
  * The key axis of every (sequence, head) is divided into split_kv chunks.
  * sk_attn_partial computes one partial output O_s and one log-sum-exp L_s per
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SK_ABI_VERSION 3
+#define SK_ABI_VERSION 4
 
 typedef enum sk_status {
     SK_OK = 0,
@@ -212,6 +213,44 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
  * skip it (the aiter page's return_lse=False). */
 sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float* lse_part,
                           const int32_t* counts, void* out, float* lse_out, void* stream);
+
+/* Backward of the merged attention (aiter page, review overview: the open
+ * item on backward coverage for split-KV long-K attention).  The forward's
+ * output is plain softmax attention over the keys each row may see, so with
+ * P = exp(scale q.k - LSE) on those keys and 0 elsewhere:
+ *   D  = rowsum(dO * O)
+ *   dS = P * (dO V^T - D)
+ *   dQ = softmax_scale dS K,  dK = softmax_scale dS^T Q,  dV = P^T dO
+ * The dQ pass splits each query block's keys as sk_attn_partial does (blocks
+ * of 128 rows, the count formula at the block's last row, split count
+ * sk_split_kv(p)) and sums the split results; dK and dV are computed per
+ * block of 128 keys over every row that sees one of them.
+ * Storage: dtype SK_BF16 or SK_F16 (SK_F32: SK_ERR_UNSUPPORTED), out_dtype
+ * must equal dtype; head dims (64, 64), (128, 128) or (192, 128).  P and dS
+ * are rounded to the storage type before their products, which accumulate in
+ * f32; the gradients are rounded to the storage type last.
+ *   q, k, v    the forward's inputs (q_/k_/v_stride_*)
+ *   out, dout  the forward's output and its gradient (o_stride_*)
+ *   lse        f32 [num_heads][rows], the LSE sk_attn_combine wrote (natural
+ *              log, -inf for a row that sees no key)
+ *   dq         same layout as q; every row of every sequence is written
+ *   dk, dv     same layouts as k and v; every key row of every sequence is
+ *              written (keys no row sees get 0); rows of a packed K/V that
+ *              belong to no sequence are left untouched
+ *   workspace  device memory of at least sk_backward_workspace_bytes(p)
+ *              bytes, 16-byte aligned; contents on entry do not matter
+ * Every tensor must be 16-byte aligned with strides that are multiples of 8
+ * elements, and the row strides of q, k, v and the outputs must not exceed
+ * 2^24 elements.  The result does not depend on split_kv beyond f32
+ * summation order. */
+sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sk_attn_backward needs for `p` on the current device
+ * (f32 D per (head, row) and one f32 dQ sum per (head, split, row, dim)), or
+ * -1 if `p` is invalid. */
+int64_t sk_backward_workspace_bytes(const sk_problem* p);
 
 #ifdef __cplusplus
 }

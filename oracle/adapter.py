@@ -13,7 +13,18 @@ from __future__ import annotations
 
 import numpy as np
 
-from .splitkv import MASK_CAUSAL, MASK_NONE, MASK_PREFIX_CAUSAL, SeqSpec, combine, partials, unsplit, valid_split_counts
+from .splitkv import (
+    MASK_CAUSAL,
+    MASK_NONE,
+    MASK_PREFIX_CAUSAL,
+    SeqSpec,
+    combine,
+    partials,
+    sampled_backward,
+    unsplit,
+    unsplit_backward,
+    valid_split_counts,
+)
 
 _MASKS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "prefix_causal": MASK_PREFIX_CAUSAL}
 
@@ -96,3 +107,30 @@ def expected(w, inputs, m_per_block: int, rows_per_seq=None, heads=None, with_un
                 d["O_ref"], d["lse_ref"] = unsplit(Q, K, V, w.softmax_scale, spec, rows)
             res[(b, h)] = d
     return res
+
+
+def _dout_slice(w, dout, b: int, h: int):
+    if w.packed:
+        q0 = int(sum(w.sq[:b]))
+        return _f64(dout[q0 : q0 + w.sq[b], h])
+    return _f64(dout[b, h])
+
+
+def backward(w, inputs, dout, heads=None):
+    """Oracle gradients of every sequence and head, keyed by (b, h):
+    dQ [sq, Dqk], dK [sk, Dqk], dV [sk, Dv] from `unsplit_backward`."""
+    heads = range(w.heads) if heads is None else heads
+    res = {}
+    for b, spec in enumerate(seq_specs(w)):
+        for h in heads:
+            Q, K, V = head_slices(w, inputs, b, h)
+            res[(b, h)] = unsplit_backward(Q, K, V, _dout_slice(w, dout, b, h), w.softmax_scale, spec)
+    return res
+
+
+def backward_sampled(w, inputs, dout, b: int, h: int, rows, keys):
+    """Oracle dQ at `rows` and dK, dV at `keys` of sequence b, head h
+    (`sampled_backward`, for sizes whose whole score matrix is too large)."""
+    spec = seq_specs(w)[b]
+    Q, K, V = head_slices(w, inputs, b, h)
+    return sampled_backward(Q, K, V, _dout_slice(w, dout, b, h), w.softmax_scale, spec, rows, keys)

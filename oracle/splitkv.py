@@ -260,6 +260,43 @@ def unsplit_backward(Q, K, V, dO, scale, spec: SeqSpec):
     return scale * (dS @ K), scale * (dS.T @ Q), P.T @ dO
 
 
+def sampled_backward(Q, K, V, dO, scale, spec: SeqSpec, rows, keys, chunk: int = 256):
+    """dQ at query rows `rows` and dK, dV at key indices `keys` of
+    `unsplit_backward`, for inputs whose whole score matrix does not fit in
+    memory.  Each step of that definition is row-wise except the sums over
+    rows that make dK and dV, so the rows are taken `chunk` at a time and those
+    two sums are added up chunk by chunk (only the f64 summation order differs
+    from `unsplit_backward`).  Q, dO: all sq rows; K, V: all sk keys."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)[: spec.sk]
+    V = np.asarray(V, dtype=np.float64)[: spec.sk]
+    dO = np.asarray(dO, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    dQ = np.zeros((len(rows), Q.shape[1]))
+    dK = np.zeros((len(keys), Q.shape[1]))
+    dV = np.zeros((len(keys), V.shape[1]))
+    all_keys = np.arange(spec.sk)
+    for c0 in range(0, spec.sq, chunk):
+        cr = np.arange(c0, min(c0 + chunk, spec.sq))
+        visible = visible_keys(cr, spec, all_keys)
+        x = np.where(visible, scale * (Q[cr] @ K.T), -np.inf)
+        has = visible.any(axis=1)
+        m = np.where(has, x.max(axis=1, initial=-np.inf), 0.0)
+        e = np.where(visible, np.exp(x - m[:, None]), 0.0)
+        z = e.sum(axis=1)
+        P = np.where(has[:, None], e / np.where(has, z, 1.0)[:, None], 0.0)
+        O = P @ V
+        D = (dO[cr] * O).sum(axis=1)
+        dS = P * (dO[cr] @ V.T - D[:, None])
+        dK += scale * (dS[:, keys].T @ Q[cr])
+        dV += P[:, keys].T @ dO[cr]
+        hit = (rows >= c0) & (rows < c0 + len(cr))
+        if hit.any():
+            dQ[hit] = scale * (dS[rows[hit] - c0] @ K)
+    return dQ, dK, dV
+
+
 def partials(Q, K, V, scale, spec: SeqSpec, m_per_block: int, rows=None):
     """Per-split partial outputs O_s [S, rows, Dv] and LSE L_s [S, rows].
 
@@ -372,6 +409,7 @@ __all__ = [
     "block_split_ranges",
     "unsplit",
     "unsplit_backward",
+    "sampled_backward",
     "partials",
     "combine",
     "split_attention",

@@ -1,4 +1,4 @@
-"""split_kv_attention_amd: split-KV attention forward for AMD Instinct MI355X.
+"""split_kv_attention_amd: split-KV attention (forward and backward) for AMD Instinct MI355X.
 
 The computation lives in libsplitkv.so (hand-written HIP kernels for gfx950,
 C ABI in include/splitkv.h).  This package is its thin Python binding:
@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     SK_ERR_HIP,
     SK_ERR_INVALID_ARG,
     SK_ERR_UNSUPPORTED,
+    SK_F16,
     SK_F32,
     SK_MASK_CAUSAL,
     SK_MASK_NONE,
@@ -22,8 +23,10 @@ from ._lib import (  # noqa: F401
     SplitKVError,
     load,
     sk_abi_version,
+    sk_attn_backward,
     sk_attn_combine,
     sk_attn_partial,
+    sk_backward_workspace_bytes,
     sk_last_error,
     sk_partial_m_per_block,
     sk_rows,

@@ -30,6 +30,8 @@ EXPORTS = (
     "sk_valid_split_counts",
     "sk_attn_partial",
     "sk_attn_combine",
+    "sk_attn_backward",
+    "sk_backward_workspace_bytes",
 )
 
 
@@ -121,6 +123,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sk_attn_partial.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sk_attn_combine.restype = ctypes.c_int
     lib.sk_attn_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.sk_attn_backward.restype = ctypes.c_int
+    lib.sk_attn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
+    lib.sk_backward_workspace_bytes.restype = ctypes.c_int64
+    lib.sk_backward_workspace_bytes.argtypes = [P]
     if path is None:
         _lib = lib
     return lib
@@ -218,5 +224,22 @@ def sk_attn_combine(problem: SkProblem, o_part, lse_part, counts, out, lse_out, 
         load().sk_attn_combine(
             ctypes.byref(problem), _ptr(o_part), _ptr(lse_part), _ptr(counts), _ptr(out), _ptr(lse_out),
             _stream(stream),
+        )
+    )
+
+
+def sk_backward_workspace_bytes(problem: SkProblem) -> int:
+    n = load().sk_backward_workspace_bytes(ctypes.byref(problem))
+    if n < 0:
+        raise SplitKVError(SK_ERR_INVALID_ARG, sk_last_error())
+    return n
+
+
+def sk_attn_backward(problem: SkProblem, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes: int,
+                     stream=None) -> None:
+    _check(
+        load().sk_attn_backward(
+            ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream),
         )
     )

@@ -6,6 +6,8 @@ enqueues the three entry points on the current stream:
 
     sk_valid_split_counts -> sk_attn_partial -> sk_attn_combine
 
+and `split_kv_attention_backward` enqueues sk_attn_backward for the gradients.
+
 Layouts: a dense batch is [B, H, S, D]; a packed variable-length batch is
 [tokens, H, D] with int32 cu_seqlens (aiter page, flash_attn_varlen_func).
 """
@@ -203,3 +205,20 @@ def split_kv_attention(q, k, v, *, return_lse: bool = True, return_partials: boo
         res.append({"counts": counts, "o_part": o_part, "lse_part": lse_part, "m_per_block": prob.m_per_block,
                     "problem": prob})
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def split_kv_attention_backward(q, k, v, out, lse, dout, **kw):
+    """dQ, dK, dV of split_kv_attention through sk_attn_backward.
+
+    `out` and `lse` are the forward's results for the same arguments (`kw` as
+    for build_problem; out_dtype must be q's dtype).  The gradients have the
+    shapes of q, k, v; a packed K/V's rows that belong to no sequence come
+    back as zeros.  The workspace is allocated with torch."""
+    prob = build_problem(q, k, v, partial_scratch=False, **kw)
+    dq = torch.empty_like(q)
+    dk = torch.zeros_like(k) if k.dim() == 3 else torch.empty_like(k)
+    dv = torch.zeros_like(v) if v.dim() == 3 else torch.empty_like(v)
+    nbytes = _lib.sk_backward_workspace_bytes(prob.c)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _lib.sk_attn_backward(prob.c, q, k, v, out, dout, lse, dq, dk, dv, ws, nbytes)
+    return dq, dk, dv

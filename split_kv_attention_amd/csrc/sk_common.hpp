@@ -218,6 +218,43 @@ __device__ __forceinline__ WorkItem decode_work(const PartialArgs& a, uint32_t b
     return it;
 }
 
+// Arguments of the backward kernels.  Gradients use the strides of the
+// tensor they belong to (dq: q's, dk: k's, dv: v's); out and dout share o's.
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;  // [H][rows], natural log, from the merge
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dvec;     // workspace: D = rowsum(dO * O), [H][rows]
+    float* dq_part;  // workspace: per-split dQ sums, [H][S_max][rows][D_qk]
+    SeqTable seqs;
+    int64_t q_row, q_head, q_batch;
+    int64_t k_row, k_head, k_batch;
+    int64_t v_row, v_head, v_batch;
+    int64_t o_row, o_head, o_batch;
+    int64_t rows;
+    int32_t heads;
+    int32_t n_qtiles;  // query blocks of the dQ kernel in the longest sequence
+    int32_t n_ktiles;  // key blocks of the dK/dV kernel in the longest sequence
+    int32_t batch;
+    float scale;
+    float scale_log2;
+};
+
+typedef hipError_t (*BackwardLauncher)(const BackwardArgs& a, hipStream_t stream);
+struct BackwardKernel {
+    BackwardLauncher launch;
+    int q_block;  // query rows per dQ block (its split partition)
+    int k_block;  // keys per dK/dV block
+};
+// Backward for (dtype, d_qk, d_v), or {nullptr, 0, 0} when not built.
+BackwardKernel find_backward(int dtype, int d_qk, int d_v);
+
 struct CountsArgs {
     int32_t* counts;
     SeqTable seqs;

@@ -188,6 +188,22 @@ sk_problem resolved(const sk_problem& p) {
     return r;
 }
 
+// Workspace of the backward: D [H][rows] f32, then the per-split dQ sums
+// [H][S_max][rows][D_qk] f32, each 256-byte aligned.
+struct BackwardLayout {
+    int64_t dvec_offset, dq_part_offset, total;
+};
+BackwardLayout backward_layout(const sk_problem& p) {
+    auto round_up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t rows = rows_of(p);
+    BackwardLayout w;
+    w.dvec_offset = 0;
+    w.dq_part_offset = round_up((int64_t)p.num_heads * rows * (int64_t)sizeof(float));
+    w.total = w.dq_part_offset +
+              round_up((int64_t)p.num_heads * p.split_kv * rows * p.head_dim_qk * (int64_t)sizeof(float));
+    return w;
+}
+
 sk_status hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(SK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -369,6 +385,97 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
     a.m_per_block = pick_partial(*p).m_per_block;  // 0 when no partial kernel exists for p
     a.pad_ = 0;
     return hip_status(sk::launch_combine(a, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
+}
+
+int64_t sk_backward_workspace_bytes(const sk_problem* p) {
+    if (check_problem(p) != SK_OK) return -1;
+    const sk_problem rp = resolved(*p);
+    ok();
+    const BackwardLayout w = backward_layout(rp);
+    return w.total;
+}
+
+sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+    sk_status st = check_problem(p);
+    if (st != SK_OK) return st;
+    const sk_problem rp = resolved(*p);
+    p = &rp;
+    if (p->dtype == SK_F32) return fail(SK_ERR_UNSUPPORTED, "the backward needs bf16 or f16 storage (got f32)");
+    if (p->out_dtype != p->dtype)
+        return fail(SK_ERR_UNSUPPORTED, "the backward needs out_dtype == dtype (got %s, %s)", dtype_name(p->dtype),
+                    dtype_name(p->out_dtype));
+    const sk::BackwardKernel kern = sk::find_backward(p->dtype, p->head_dim_qk, p->head_dim_v);
+    if (!kern.launch)
+        return fail(SK_ERR_UNSUPPORTED, "no backward kernel for dtype %s with head dims (%d, %d)", dtype_name(p->dtype),
+                    p->head_dim_qk, p->head_dim_v);
+    const int64_t rows = rows_of(*p);
+    if (p->batch == 0) return ok();
+    if (workspace_bytes < 0) return fail(SK_ERR_INVALID_ARG, "workspace_bytes must be >= 0");
+    const BackwardLayout w = backward_layout(*p);
+    if (w.total > 0 && (!workspace || workspace_bytes < w.total))
+        return fail(SK_ERR_INVALID_ARG, "workspace needs %lld bytes (got %lld)", (long long)w.total,
+                    (long long)workspace_bytes);
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return fail(SK_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    // 16-byte vector loads of 16-bit rows; 8-byte stores of the gradients.
+    const int64_t strides[] = {p->q_stride_row, p->q_stride_head, p->q_stride_batch, p->k_stride_row,
+                               p->k_stride_head, p->k_stride_batch, p->v_stride_row, p->v_stride_head,
+                               p->v_stride_batch, p->o_stride_row, p->o_stride_head, p->o_stride_batch};
+    for (int64_t s : strides)
+        if (s % 8) return fail(SK_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    for (const void* x : ptrs)
+        if (x && !aligned(x, 16)) return fail(SK_ERR_UNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(SK_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    // Tiles are addressed with 32-bit byte offsets from their first row.
+    const int64_t row_strides[] = {p->q_stride_row, p->k_stride_row, p->v_stride_row, p->o_stride_row};
+    for (int64_t s : row_strides)
+        if (s > ((int64_t)1 << 24)) return fail(SK_ERR_UNSUPPORTED, "row strides above 2^24 elements are not supported");
+    if (p->batch > 65535 || p->num_heads > 65535)
+        return fail(SK_ERR_UNSUPPORTED, "batch and num_heads above 65535 are not supported by the backward");
+    const int64_t n_qtiles = ((int64_t)p->max_seqlen_q + kern.q_block - 1) / kern.q_block;
+    const int64_t n_ktiles = ((int64_t)p->max_seqlen_k + kern.k_block - 1) / kern.k_block;
+    if (n_qtiles * p->num_heads * p->split_kv * p->batch >= ((int64_t)1 << 31) ||
+        n_ktiles * p->num_heads * p->batch >= ((int64_t)1 << 31) ||
+        ((int64_t)p->max_seqlen_q * (p->head_dim_qk / 4) + 255) / 256 > 0x7fffffff)
+        return fail(SK_ERR_UNSUPPORTED, "problem too large for the backward grids");
+    if ((p->max_seqlen_q == 0 || rows == 0) && p->max_seqlen_k == 0) return ok();
+
+    sk::BackwardArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dvec = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.dvec_offset);
+    a.dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.dq_part_offset);
+    a.seqs = seq_table(*p);
+    a.q_row = p->q_stride_row;
+    a.q_head = p->q_stride_head;
+    a.q_batch = p->q_stride_batch;
+    a.k_row = p->k_stride_row;
+    a.k_head = p->k_stride_head;
+    a.k_batch = p->k_stride_batch;
+    a.v_row = p->v_stride_row;
+    a.v_head = p->v_stride_head;
+    a.v_batch = p->v_stride_batch;
+    a.o_row = p->o_stride_row;
+    a.o_head = p->o_stride_head;
+    a.o_batch = p->o_stride_batch;
+    a.rows = rows;
+    a.heads = p->num_heads;
+    a.n_qtiles = (int32_t)n_qtiles;
+    a.n_ktiles = (int32_t)n_ktiles;
+    a.batch = p->batch;
+    a.scale = p->softmax_scale;
+    a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    return hip_status(kern.launch(a, (hipStream_t)stream), "backward kernel launch");
 }
 
 }  // extern "C"

@@ -126,6 +126,14 @@ def make_inputs(w: Workload, device, seed: int = 0) -> dict:
     return out
 
 
+def make_dout(w: Workload, device, seed: int = 0):
+    """Output gradient dO, N(0, 1) in the workload dtype, shaped like the
+    output: [B, H, Sq, D_v] dense, [tokens, H, D_v] packed."""
+    shape = (sum(w.sq), w.heads, w.d_v) if w.packed else (w.batch, w.heads, w.sq[0], w.d_v)
+    x = torch.randn(shape, generator=_gen(device, seed, 3), device=device, dtype=torch.float32)
+    return x.to(w.torch_dtype) if w.torch_dtype != torch.float32 else x
+
+
 def problem_kwargs(w: Workload, inputs: dict) -> dict:
     """Keyword arguments of attention.build_problem for workload `w`."""
     kw = dict(

@@ -93,6 +93,7 @@ def _all_calls(p):
         lib.sk_valid_split_counts(pp, FAKE, None),
         lib.sk_attn_partial(pp, FAKE, FAKE, FAKE, FAKE, FAKE, None),
         lib.sk_attn_combine(pp, FAKE, FAKE, FAKE, FAKE, FAKE, None),
+        lib.sk_attn_backward(pp, *([FAKE] * 10), 1 << 40, None),
     ]
 
 
@@ -186,10 +187,43 @@ def test_empty_problems_are_no_ops():
     """Nothing to do (no sequence, or no query row) is success, with no launch."""
     p = _good()
     p.batch = 0
-    assert _all_calls(p) == [sk.SK_OK] * 3
+    assert _all_calls(p) == [sk.SK_OK] * 4
     p = _good()
     p.max_seqlen_q = 0
-    assert _all_calls(p) == [sk.SK_OK] * 3
+    assert _all_calls(p)[:3] == [sk.SK_OK] * 3  # the backward still zeroes dK, dV
+    p.max_seqlen_k = 0
+    assert _all_calls(p)[3] == sk.SK_OK
+
+
+def _backward(p, ws=FAKE, ws_bytes=1 << 40, **ptrs):
+    args = {n: FAKE for n in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv")}
+    args.update(ptrs)
+    return _lib.load().sk_attn_backward(ctypes.byref(p), *args.values(), ws, ws_bytes, None)
+
+
+def test_backward_workspace_and_host_checks():
+    p = _good()  # H = 4, S = 4, 200 rows, D_qk = 128
+    assert sk.sk_backward_workspace_bytes(p) == 3328 + 4 * 4 * 200 * 128 * 4  # D (256-aligned), then dQ sums
+    p.num_heads = 0
+    with pytest.raises(sk.SplitKVError):
+        sk.sk_backward_workspace_bytes(p)
+    for field, value in (("dtype", sk.SK_F32), ("out_dtype", _lib.SK_F16), ("head_dim_qk", 96),
+                         ("q_stride_row", 132)):
+        p = _good()
+        setattr(p, field, value)
+        if field == "dtype":
+            p.out_dtype = sk.SK_F32
+        assert _backward(p) == sk.SK_ERR_UNSUPPORTED, field
+    p = _good()
+    need = sk.sk_backward_workspace_bytes(p)
+    assert _backward(p, ws_bytes=need - 1) == sk.SK_ERR_INVALID_ARG
+    assert "workspace" in sk.sk_last_error()
+    assert _backward(p, ws=None, ws_bytes=need) == sk.SK_ERR_INVALID_ARG
+    assert _backward(p, ws_bytes=-1) == sk.SK_ERR_INVALID_ARG
+    assert _backward(p, dq=None) == sk.SK_ERR_INVALID_ARG
+    assert _backward(p, dk=FAKE + 8) == sk.SK_ERR_UNSUPPORTED
+    assert _backward(p, ws=FAKE + 8) == sk.SK_ERR_UNSUPPORTED
+    assert _backward(p, lse=FAKE + 2) == sk.SK_ERR_INVALID_ARG
 
 
 def test_status_strings():

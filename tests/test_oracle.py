@@ -246,6 +246,29 @@ def test_backward_matches_finite_differences():
         assert abs((fp - fm) / (2 * h) - grads[which][i, j]) < 1e-7
 
 
+@pytest.mark.parametrize("mask,off,win", [(MASK_NONE, 0, -1), (MASK_PREFIX_CAUSAL, 20, 9), (MASK_CAUSAL, 0, -1)])
+def test_sampled_backward_matches_torch_autograd_f64(mask, off, win):
+    """The chunked form used at full size: rows spread over several chunks
+    (including a ragged last one), against torch autograd through float64
+    SDPA with the explicit visibility mask."""
+    rng = np.random.default_rng(43)
+    sq, sk, d, dv = 37, 50, 5, 4
+    Q, K, V, dO = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, dv), _rand(rng, sq, dv)
+    spec = SeqSpec(sq, sk, 2, 4, mask, off, window_left=win)
+    rows = np.array([0, 1, 7, 8, 9, 30, 36])
+    keys = np.array([0, 5, 17, 31, 49])
+    dQ, dK, dV = oracle.sampled_backward(Q, K, V, dO, 0.45, spec, rows, keys, chunk=8)
+    vis = torch.from_numpy(osk.visible_keys(np.arange(sq), spec, np.arange(sk)))
+    has = vis.any(dim=1)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_() for a in (Q, K, V))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[has][None, None], tk[None, None], tv[None, None], attn_mask=vis[has][None, None], scale=0.45)[0, 0]
+    o.backward(torch.from_numpy(dO)[has])
+    np.testing.assert_allclose(dQ, tq.grad.numpy()[rows], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dK, tk.grad.numpy()[keys], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dV, tv.grad.numpy()[keys], rtol=1e-11, atol=1e-12)
+
+
 def test_block_populated_splits_hold_every_key_the_block_sees():
     """Real early exit: the splits a block still writes (populated) include
     every split holding a key that any row of the block sees, and every other
