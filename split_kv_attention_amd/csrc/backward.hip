@@ -60,8 +60,24 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
     *reinterpret_cast<t4*>(p) = r;
 }
 
+// Swizzle of the 16-byte chunks of a tile row for tiles read both ways: with
+// 64 banks of 4 bytes, a 16-byte row read serves 16 lanes (16 rows, one
+// chunk each) per cycle and a transposed 8-byte read 32 lanes (4 rows x 4
+// consecutive chunks) per cycle.  Rows of 16 chunks all start in bank 0, so
+// the XOR must make 16 consecutive rows distinct and give 4 consecutive rows
+// different bits 2..3; rows of 8 or 24 chunks alternate between banks 0 and
+// 32, so it must make the 8 even (and the 8 odd) rows of 16 distinct and give
+// the two even (two odd) rows of 4 a different bit 2.  Both stay inside the
+// row (XOR below 16 for 16 chunks, below 8 for 8 or 24) and repeat every 16
+// rows.
+template <int CH>
+__device__ __forceinline__ int bt_swz(int r, int c) {
+    if constexpr (CH % 16 == 0) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 // Reads of a row-major [rows][D] 16-bit tile in LDS whose 16-byte chunks are
-// swizzled with k_swz<D/8>: (a) the A operand of a 32x32x16 MFMA with the
+// swizzled with bt_swz<D/8>: (a) the A operand of a 32x32x16 MFMA with the
 // tile's rows as M (lane = row col, 8 consecutive D entries from k-step t),
 // (b) the A operand with D as M and the rows as K, read transposed with
 // ds_read_b64_tr_b16 in the row order the accumulator-to-B-operand mapping
@@ -79,15 +95,15 @@ struct TileReads {
     __device__ __forceinline__ void init(const uint16_t* tile, int lane) {
         const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-        for (int m = 0; m < kSpan; ++m) row_addr[m] = lds_addr(tile + col * D + k_swz<CH>(col, 2 * m + half) * 8);
+        for (int m = 0; m < kSpan; ++m) row_addr[m] = lds_addr(tile + col * D + bt_swz<CH>(col, 2 * m + half) * 8);
         const int s16 = lane & 15, g2 = (lane >> 4) & 1;
         const int r_a = half * 4 + (s16 >> 2);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
             const int q = 4 * c + 2 * g2 + ((s16 & 3) >> 1);
             const int in = (s16 & 1) * 4;
-            tr_addr[c][0] = lds_addr(tile + r_a * D + k_swz<CH>(r_a, q) * 8 + in);
-            tr_addr[c][1] = lds_addr(tile + (r_a + 8) * D + k_swz<CH>(r_a + 8, q) * 8 + in);
+            tr_addr[c][0] = lds_addr(tile + r_a * D + bt_swz<CH>(r_a, q) * 8 + in);
+            tr_addr[c][1] = lds_addr(tile + (r_a + 8) * D + bt_swz<CH>(r_a + 8, q) * 8 + in);
         }
     }
 };
@@ -246,7 +262,6 @@ void bwd_dq_kernel(BackwardArgs a) {
     const int lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int qrow = r0 + wave * 32 + col;
     const bool row_ok = qrow < sq.sq;
-    const bool wave_active = (r0 + wave * 32) < sq.sq;
     const int64_t prow = sq.row0 + qrow;
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
     const int lo_q = (int)min(vis_first(sq, win, qrow), (int64_t)0x7fffffff);
@@ -285,12 +300,12 @@ void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i) {
         const int P = i * kThreads + tid, r = P / (DQK / 8);
-        k_off[i] = (uint32_t)(r * a.k_row + k_swz<DQK / 8>(r, P % (DQK / 8)) * 8) * 2u;
+        k_off[i] = (uint32_t)(r * a.k_row + bt_swz<DQK / 8>(r, P % (DQK / 8)) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
         const int P = i * kThreads + tid, r = P / (DV / 8);
-        v_off[i] = (uint32_t)(r * a.v_row + k_swz<DV / 8>(r, P % (DV / 8)) * 8) * 2u;
+        v_off[i] = (uint32_t)(r * a.v_row + bt_swz<DV / 8>(r, P % (DV / 8)) * 8) * 2u;
     }
     uint16_t* const Ks = smem;
     uint16_t* const Vs = smem + 2 * C::K_ELEMS;
@@ -360,21 +375,25 @@ void bwd_dq_kernel(BackwardArgs a) {
         gemm_tr_step<E, DQK, KO + 3 * 16 * DQK * 2>(kr, dq, ds[1][1]);
     };
 
+    // Tiles alternate between the two LDS slots; the loop takes them in
+    // pairs so that each step's slot is a constant and the accumulators flow
+    // through straight-line code.  A wave past the sequence's last row runs
+    // on zero rows (its P is 0) instead of branching around the step.
     const int ntiles = ks < ke ? (ke - ks + kKT - 1) / kKT : 0;
     if (ntiles > 0) {
         issue(ks, 0);
         sync_tiles();
-        for (int i = 0; i < ntiles; ++i) {
+        int i = 0;
+        for (; i + 2 <= ntiles; i += 2) {
             const int kt = ks + i * kKT;
-            if (i + 1 < ntiles) issue(kt + kKT, (i + 1) & 1);
-            if (wave_active) {
-                if (i & 1)
-                    step(kt, std::integral_constant<int, 1>{});
-                else
-                    step(kt, std::integral_constant<int, 0>{});
-            }
+            issue(kt + kKT, 1);
+            step(kt, std::integral_constant<int, 0>{});
+            sync_tiles();
+            if (i + 2 < ntiles) issue(kt + 2 * kKT, 0);
+            step(kt + kKT, std::integral_constant<int, 1>{});
             sync_tiles();
         }
+        if (i < ntiles) step(ks + i * kKT, std::integral_constant<int, 0>{});
     }
 
     if (!row_ok || prow >= a.rows) return;
@@ -488,10 +507,32 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         if (win >= 0) hi = min(hi, (int64_t)k1 - sq.off + win);
         q_hi = (int)max(hi, (int64_t)q_lo);
     }
-    // This lane's key is visible to rows q in [qmin, qmax].
-    const int64_t qmin = mask == SK_MASK_NONE ? 0 : (int64_t)key - sq.off;
-    const int64_t qmax = win >= 0 ? (int64_t)key - sq.off + win : (int64_t)0x7fffffff;
-    const bool key_vis = key_ok && key <= sq.lv;
+    // This lane's key is visible to rows q in [q_first, q_first + q_span]
+    // (q_span as unsigned: q is visible iff (unsigned)(q - q_first) <= q_span);
+    // a key no row sees gets q_first = 2^31, q_span = 0, which no q < 2^31 meets.
+    uint32_t q_first = 0x80000000u, q_span = 0;
+    {
+        const int64_t lo = mask == SK_MASK_NONE ? 0 : max((int64_t)0, (int64_t)key - sq.off);
+        const int64_t hi = min((int64_t)sq.sq - 1, win >= 0 ? (int64_t)key - sq.off + win : (int64_t)sq.sq);
+        if (key_ok && key <= sq.lv && lo <= hi) {
+            q_first = (uint32_t)lo;
+            q_span = (uint32_t)(hi - lo);
+        }
+    }
+    // Rows [full_lo, full_hi] see every key of the block: a tile inside them
+    // needs no mask (uniform over the workgroup).
+    int full_lo = 1, full_hi = 0;
+    {
+        const int64_t kl = (int64_t)k0 + kKB - 1;  // the block's last key
+        if (kl < sq.sk && kl <= sq.lv) {
+            const int64_t lo = mask == SK_MASK_NONE ? 0 : max((int64_t)0, kl - sq.off);
+            const int64_t hi = min((int64_t)sq.sq - 1, win >= 0 ? (int64_t)k0 - sq.off + win : (int64_t)sq.sq);
+            if (lo <= hi) {
+                full_lo = (int)lo;
+                full_hi = (int)hi;
+            }
+        }
+    }
 
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q) +
                             (a.seqs.cu_q ? sq.row0 * a.q_row : (int64_t)b * a.q_batch) + (int64_t)head * a.q_head;
@@ -501,12 +542,12 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
     for (int i = 0; i < C::Q_LOADS; ++i) {
         const int P = i * kThreads + tid, r = P / (DQK / 8);
-        q_off[i] = (uint32_t)(r * a.q_row + k_swz<DQK / 8>(r, P % (DQK / 8)) * 8) * 2u;
+        q_off[i] = (uint32_t)(r * a.q_row + bt_swz<DQK / 8>(r, P % (DQK / 8)) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::O_LOADS; ++i) {
         const int P = i * kThreads + tid, r = P / (DV / 8);
-        o_off[i] = (uint32_t)(r * a.o_row + k_swz<DV / 8>(r, P % (DV / 8)) * 8) * 2u;
+        o_off[i] = (uint32_t)(r * a.o_row + bt_swz<DV / 8>(r, P % (DV / 8)) * 8) * 2u;
     }
     uint16_t* const Qs = smem;
     uint16_t* const Os = smem + 2 * C::Q_ELEMS;
@@ -553,8 +594,14 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
         gemm_rows1<E, DQK, QO>(qr, s, kf);  // S = Q K^T (this lane: one key, 16 rows)
         gemm_rows1<E, DV, OO>(orr, dp, vf);  // dP = dO V^T
-        // this lane holds rows 8 (j / 4) + 4 half + j % 4; their LSE and D
-        // come four at a time
+        // this lane holds rows qt + 8 (j / 4) + 4 half + j % 4
+        if (!(qt >= full_lo && qt + kQT - 1 <= full_hi)) {
+            const uint32_t base = (uint32_t)(qt + half * 4) - q_first;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (base + (uint32_t)((j >> 2) * 8 + (j & 3)) > q_span) s[j] = -INFINITY;
+        }
+        // P and dS; the rows' LSE and D come four at a time
         v8 pf[2], dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -564,9 +611,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * g + i;
-                const int q = qt + g * 8 + half * 4 + i;
-                const bool vis = key_vis && q >= qmin && q <= qmax && q < sq.sq;
-                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[j], cl2, -l2[i])) : 0.f;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[j], cl2, -l2[i]));
                 pf[j >> 3][j & 7] = (T)pv;
                 dsf[j >> 3][j & 7] = (T)(pv * (dp[j] - dd[i]));
             }
@@ -578,19 +623,23 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         gemm_tr_step<E, DQK, QO + 16 * DQK * 2>(qr, dk, dsf[1]);
     };
 
+    // Tiles in pairs over the two LDS slots (constant slot per step, no
+    // branch around the accumulators).
     const int ntiles = q_hi > q_lo ? (q_hi - q_lo + kQT - 1) / kQT : 0;
     if (ntiles > 0) {
         issue(q_lo, 0);
         sync_tiles(0);
-        for (int i = 0; i < ntiles; ++i) {
+        int i = 0;
+        for (; i + 2 <= ntiles; i += 2) {
             const int qt = q_lo + i * kQT;
-            if (i + 1 < ntiles) issue(qt + kQT, (i + 1) & 1);
-            if (i & 1)
-                step(qt, std::integral_constant<int, 1>{});
-            else
-                step(qt, std::integral_constant<int, 0>{});
-            sync_tiles((i + 1) & 1);
+            issue(qt + kQT, 1);
+            step(qt, std::integral_constant<int, 0>{});
+            sync_tiles(1);
+            if (i + 2 < ntiles) issue(qt + 2 * kQT, 0);
+            step(qt + kQT, std::integral_constant<int, 1>{});
+            sync_tiles(0);
         }
+        if (i < ntiles) step(q_lo + i * kQT, std::integral_constant<int, 0>{});
     }
 
     if (!key_ok) return;
