@@ -4,9 +4,12 @@ Workload: the long-context packed-varlen prefill (one sequence, H = 12,
 Sq = 4096, Sk = 42700, D_qk = 192, D_v = 128, split_kv = 3, non-causal, bf16
 inputs N(0, 1) from a seeded generator, scale 1/sqrt(192)).  A step is the
 whole path: sk_valid_split_counts -> sk_attn_partial -> sk_attn_combine, with
-inputs already resident in HBM.  Prints ONE JSON line.
+inputs already resident in HBM.  Prints ONE JSON line.  After the timed
+forward steps, the backward (sk_attn_backward: dQ, dK, dV of the same
+problem for a seeded dO) is timed on its own and reported under "backward".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--backward-steps N]
 """
 from __future__ import annotations
 
@@ -27,8 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_hbm_traffic.json")
 # the partial entry point's kernels and the host code that plans their launch
-PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/sk_common.hpp",
-                   "split_kv_attention_amd/csrc/splitkv_api.cpp"]
+PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/mfma_common.hpp",
+                   "split_kv_attention_amd/csrc/sk_common.hpp", "split_kv_attention_amd/csrc/splitkv_api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -88,6 +91,58 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
     }
 
 
+def time_backward(w, prob, inputs, out, lse, stream, steps: int):
+    """sk_attn_backward on the forward's out / LSE and a seeded dO, timed
+    with HIP events on `stream` over `steps` calls after 2 warmup calls.
+
+    FLOPs: the five products of attention's gradient over the Sq x Sk pairs
+    (recomputed scores Q K^T and dO V^T, dV = P^T dO, dQ = dS K,
+    dK = dS^T Q), 2 Sq Sk H (3 D_qk + 2 D_v).  The kernels compute the scores
+    and dO V^T twice (once in the dQ pass, once in the dK/dV pass):
+    2 Sq Sk H (4 D_qk + 3 D_v) executed."""
+    import torch
+
+    from split_kv_attention_amd import _lib, workloads
+
+    q, k, v = inputs["q"], inputs["k"], inputs["v"]
+    dout = workloads.make_dout(w, q.device, 3)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = _lib.sk_backward_workspace_bytes(prob.c)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    sh = stream.cuda_stream
+
+    def call():
+        _lib.sk_attn_backward(prob.c, q, k, v, out, dout, lse, dq, dk, dv, ws, nbytes, sh)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    H, Sq, Sk = w.heads, w.sq[0], w.sk[0]
+    flop = 2.0 * Sq * Sk * H * (3 * w.d_qk + 2 * w.d_v)
+    executed = 2.0 * Sq * Sk * H * (4 * w.d_qk + 3 * w.d_v)
+    achieved = flop / (ms * 1e-3) / 1e12
+    return {
+        "bound": "mfma",
+        "kernels": "bwd_rowdot, bwd_dq (per split), bwd_dkdv, bwd_dq_reduce",
+        "ms": ms,
+        "calls": steps,
+        "algorithmic_flop": flop,
+        "executed_flop": executed,
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": achieved / PEAK_BF16_TFLOPS,
+        "workspace_bytes": nbytes,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +150,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10, help="combine timings after a cache flush")
+    ap.add_argument("--backward-steps", type=int, default=10, help="timed backward calls (0: skip)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -162,6 +218,10 @@ def main() -> int:
     t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
     del flush
 
+    backward = None
+    if args.backward_steps > 0:
+        backward = time_backward(w, prob, inputs, out, lse_out, stream, args.backward_steps)
+
     if args.copy_check:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -222,6 +282,7 @@ def main() -> int:
         },
         "counts_ms": t_counts,
         "attention_tflops_partial_plus_combine": flops / ((t_partial + t_combine) * 1e-3) / 1e12,
+        "backward": backward,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -108,85 +108,96 @@ struct TileReads {
     }
 };
 
-// acc[rb] += A(rows 32 rb .. of the tile, via reads (a)) * B[t] over the
-// D / 16 k-steps; the next step's fragments are read before this step's
-// MFMAs.  NRB: 32-row blocks (1 or 2).
-template <typename E, int D, int NRB, int SLOT_OFS>
-__device__ __forceinline__ void gemm_rows(const TileReads<D>& tr, f32x16 (&acc)[NRB], const typename E::v8 (&b)[D / 16]) {
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, N>{});
+}
+
+// acc[rb] += A(rows 32 rb .. 32 rb + 31 of the tile, reads (a)) * b[t] over
+// the D / 16 k-steps.  PF k-steps of reads are in flight ahead of the MFMAs
+// (one LDS read takes longer than the one or two MFMAs of a step); the reads
+// go to a ring of PF + 1 buffers, so a buffer is refilled one step after the
+// MFMA that read it.  side(t) runs after step t's MFMAs are issued.
+template <typename E, int D, int NRB, int SLOT_OFS, int PF, typename Side>
+__device__ __forceinline__ void gemm_rows(const TileReads<D>& tr, f32x16 (&acc)[NRB], const typename E::v8 (&b)[D / 16],
+                                          Side&& side) {
     using v8 = typename E::v8;
     constexpr int kSpan = TileReads<D>::kSpan;
     constexpr int kSteps = D / 16;
-    static_assert(NRB == 2, "two 32-row blocks per read pair");
-    i32x4_t f[2][2];
-    auto rd = [&](i32x4_t(&x)[2], auto t_c) {
+    constexpr int P = PF < kSteps ? PF : kSteps;
+    constexpr int R = P + 1;
+    i32x4_t f[R][NRB];
+    auto rd = [&](auto t_c) {
         constexpr int t = decltype(t_c)::value;
-        x[0] = k_read<SLOT_OFS + (t / kSpan) * kSpan * 32>(tr.row_addr[t % kSpan]);
-        x[1] = k_read<SLOT_OFS + (t / kSpan) * kSpan * 32 + 32 * D * 2>(tr.row_addr[t % kSpan]);
+        static_for<NRB>([&](auto rb_c) {
+            constexpr int rb = decltype(rb_c)::value;
+            f[t % R][rb] = k_read<SLOT_OFS + (t / kSpan) * kSpan * 32 + rb * 32 * D * 2>(tr.row_addr[t % kSpan]);
+        });
     };
-    rd(f[0], std::integral_constant<int, 0>{});
-    [&]<int... Step>(std::integer_sequence<int, Step...>) {
-        (([&] {
-            constexpr int t = Step;
-            if constexpr (t + 1 < kSteps) {
-                rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
-                k_wait<2>(f[t & 1][0], f[t & 1][1]);
-            } else {
-                k_wait<0>(f[t & 1][0], f[t & 1][1]);
-            }
-            acc[0] = E::mfma(__builtin_bit_cast(v8, f[t & 1][0]), b[t], acc[0]);
-            acc[1] = E::mfma(__builtin_bit_cast(v8, f[t & 1][1]), b[t], acc[1]);
-        }()),
-         ...);
-    }(std::make_integer_sequence<int, kSteps>{});
-}
-
-// Same for a single 32-row block.
-template <typename E, int D, int SLOT_OFS>
-__device__ __forceinline__ void gemm_rows1(const TileReads<D>& tr, f32x16& acc, const typename E::v8 (&b)[D / 16]) {
-    using v8 = typename E::v8;
-    constexpr int kSpan = TileReads<D>::kSpan;
-    constexpr int kSteps = D / 16;
-    i32x4_t f[2][2];
-    auto rd = [&](i32x4_t(&x)[2], auto t_c) {
+    static_for<P>(rd);
+    static_for<kSteps>([&](auto t_c) {
         constexpr int t = decltype(t_c)::value;
-        x[0] = k_read<SLOT_OFS + (t / kSpan) * kSpan * 32>(tr.row_addr[t % kSpan]);
-    };
-    rd(f[0], std::integral_constant<int, 0>{});
-    [&]<int... Step>(std::integer_sequence<int, Step...>) {
-        (([&] {
-            constexpr int t = Step;
-            if constexpr (t + 1 < kSteps) {
-                rd(f[(t + 1) & 1], std::integral_constant<int, t + 1>{});
-                asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(f[t & 1][0]));
-            } else {
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[t & 1][0]));
-            }
-            acc = E::mfma(__builtin_bit_cast(v8, f[t & 1][0]), b[t], acc);
-        }()),
-         ...);
-    }(std::make_integer_sequence<int, kSteps>{});
-}
-
-// out[c] += A^T(read transposed from the tile, rows 32 kb + ..) * B for one
-// step (kb, u) of 16 tile rows, for every 32-column block c of D.
-template <typename E, int D, int OFS>
-__device__ __forceinline__ void gemm_tr_step(const TileReads<D>& tr, f32x16 (&out)[D / 32], const typename E::v8& b) {
-    using v8 = typename E::v8;
-    constexpr int NB = D / 32;
-    s16x4 x[2 * NB];
+        // reads issued after step t's so far: steps t + 1 .. min(t + P - 1, kSteps - 1)
+        constexpr int later = ((t + P - 1 < kSteps - 1) ? (t + P - 1) : (kSteps - 1)) - t;
+        static_assert(later * NRB <= 15, "lgkmcnt range");
+        i32x4_t(&x)[NRB] = f[t % R];
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(later * NRB) : "memory");
 #pragma unroll
-    for (int c = 0; c < NB; ++c) {
+        for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(x[rb]));  // no use above the wait
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) acc[rb] = E::mfma(__builtin_bit_cast(v8, x[rb]), b[t], acc[rb]);
+        if constexpr (t + P < kSteps) rd(std::integral_constant<int, t + P>{});
+        side(t_c);
+    });
+}
+
+struct NoSide {
+    template <typename T>
+    __device__ __forceinline__ void operator()(T) const {}
+};
+
+// Transposed reads of one step (16 tile rows at byte offset OFS) for every
+// 32-column block c of D into x[2 c], x[2 c + 1].
+template <int D, int OFS, int N>
+__device__ __forceinline__ void tr_issue(const TileReads<D>& tr, s16x4 (&x)[N]) {
+    static_assert(2 * (D / 32) <= N, "read buffer");
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
         x[2 * c] = tr_read<OFS>(tr.tr_addr[c][0]);
         x[2 * c + 1] = tr_read<OFS>(tr.tr_addr[c][1]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// out[c] += A^T(x) * b for every 32-column block c of D, once at most LATER
+// LDS reads (the ones issued after x's) are outstanding; side(c) runs after
+// the MFMA of block c is issued, so that VALU work fills the MFMA pipe's
+// time.
+template <typename E, int D, int LATER, int N, typename Side>
+__device__ __forceinline__ void tr_mfma(s16x4 (&x)[N], f32x16 (&out)[D / 32], const typename E::v8& b, Side&& side) {
+    using v8 = typename E::v8;
+    constexpr int NB = D / 32;
+    static_assert(LATER <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(LATER) : "memory");
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) asm volatile("" : "+v"(x[i]));  // no use above the wait
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
+    static_for<NB>([&](auto c_c) {
+        constexpr int c = decltype(c_c)::value;
         const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(x[2 * c], x[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         out[c] = E::mfma(a, b, out[c]);
-    }
+        side(c_c);
+    });
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs (block b runs on XCD
+// b % 8); this renumbering gives each XCD one contiguous range of logical
+// blocks, so the blocks that share K/V (dQ: the query tiles of one split) or
+// Q/dO (dK/dV: the key blocks of one head) share one L2.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t nb) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t x = b % kXcds;
+    return x * (nb / kXcds) + min(x, nb % kXcds) + b / kXcds;
 }
 
 // ---------------------------------------------------------------------------
@@ -236,7 +247,7 @@ void bwd_dq_kernel(BackwardArgs a) {
     using v8 = typename E::v8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::K_ELEMS + C::V_ELEMS)];
 
-    uint32_t w = blockIdx.x;
+    uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
     const int tile = (int)(w % a.n_qtiles);
     w /= a.n_qtiles;
     const int head = (int)(w % a.heads);
@@ -342,14 +353,13 @@ void bwd_dq_kernel(BackwardArgs a) {
     auto step = [&](int kt, auto slot_c) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int KO = slot * C::K_ELEMS * 2, VO = slot * C::V_ELEMS * 2;  // slot byte offsets
+        constexpr int NB = DQK / 32;
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
-        gemm_rows<E, DQK, 2, KO>(kr, s, qf);  // S^T = K Q^T
-        gemm_rows<E, DV, 2, VO>(vr, dp, df);  // dP^T = V dO^T
+        gemm_rows<E, DQK, 2, KO, 3>(kr, s, qf, NoSide{});  // S^T = K Q^T
         if (kt >= full_end || kt < full_start) {
-            asm volatile("");
             const int lim = min(ke - 1, vis_q) - kt - half * 4, first = lo_q - kt - half * 4;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -359,20 +369,39 @@ void bwd_dq_kernel(BackwardArgs a) {
                     if (rel > lim || rel < first) s[kb][j] = -INFINITY;
                 }
         }
-        // dS^T = P^T * (dP^T - D), rounded to the storage type in GEMM1's B layout
+        // dP^T = V dO^T; meanwhile P^T = exp2(S^T scale log2e - LSE log2e)
+        // replaces S^T, 32 / (D_v / 16) elements per k-step
+        gemm_rows<E, DV, 2, VO, 3>(vr, dp, df, [&](auto t_c) {
+            constexpr int t = decltype(t_c)::value, per = 32 / (DV / 16);
+#pragma unroll
+            for (int e = t * per; e < (t + 1) * per; ++e)
+                s[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], cl2, -lse2));
+        });
+        // dS^T = P^T * (dP^T - D) in GEMM1's B layout; dQ^T += K^T dS^T over
+        // the tile's 64 keys in four steps of 16, each step's K^T reads
+        // issued before the previous step's MFMAs and the next dS slice
+        // computed under them
         v8 ds[2][2];
+        auto ds_slice = [&](int kb, int h) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][j], cl2, -lse2));
-                ds[kb][j >> 3][j & 7] = (T)(pv * (dp[kb][j] - dval));
-            }
-        // dQ^T += K^T dS^T over the tile's 64 keys
-        gemm_tr_step<E, DQK, KO + 0 * 16 * DQK * 2>(kr, dq, ds[0][0]);
-        gemm_tr_step<E, DQK, KO + 1 * 16 * DQK * 2>(kr, dq, ds[0][1]);
-        gemm_tr_step<E, DQK, KO + 2 * 16 * DQK * 2>(kr, dq, ds[1][0]);
-        gemm_tr_step<E, DQK, KO + 3 * 16 * DQK * 2>(kr, dq, ds[1][1]);
+            for (int j = 0; j < 8; ++j) ds[kb][h][j] = (T)(s[kb][8 * h + j] * (dp[kb][8 * h + j] - dval));
+        };
+        s16x4 xa[2 * NB], xb[2 * NB];
+        tr_issue<DQK, KO + 0 * 16 * DQK * 2>(kr, xa);
+        ds_slice(0, 0);
+        tr_issue<DQK, KO + 1 * 16 * DQK * 2>(kr, xb);
+        tr_mfma<E, DQK, 2 * NB>(xa, dq, ds[0][0], [&](auto c_c) {
+            if constexpr (decltype(c_c)::value == 0) ds_slice(0, 1);
+        });
+        tr_issue<DQK, KO + 2 * 16 * DQK * 2>(kr, xa);
+        tr_mfma<E, DQK, 2 * NB>(xb, dq, ds[0][1], [&](auto c_c) {
+            if constexpr (decltype(c_c)::value == 0) ds_slice(1, 0);
+        });
+        tr_issue<DQK, KO + 3 * 16 * DQK * 2>(kr, xb);
+        tr_mfma<E, DQK, 2 * NB>(xa, dq, ds[1][0], [&](auto c_c) {
+            if constexpr (decltype(c_c)::value == 0) ds_slice(1, 1);
+        });
+        tr_mfma<E, DQK, 0>(xb, dq, ds[1][1], NoSide{});
     };
 
     // Tiles alternate between the two LDS slots; the loop takes them in
@@ -454,7 +483,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(16))) float row_lse2[2][kQT];
     __shared__ __attribute__((aligned(16))) float row_d[2][kQT];
 
-    uint32_t w = blockIdx.x;
+    uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
     const int ktile = (int)(w % a.n_ktiles);
     w /= a.n_ktiles;
     const int head = (int)(w % a.heads);
@@ -553,7 +582,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     uint16_t* const Os = smem + 2 * C::Q_ELEMS;
     const float* lse_h = a.lse + (int64_t)head * a.rows + sq.row0;
     const float* d_h = a.dvec + (int64_t)head * a.rows + sq.row0;
-    float pre_l = 0.f, pre_d = 0.f;  // this thread's row value of the next tile (threads 0..31)
+    float pre_l = -INFINITY, pre_d = 0.f;  // this thread's row values of the next tile (threads 0..31)
     auto issue = [&](int qt, int slot) {
         const int rows = min(sq.sq - qt, kQT);
         const uint32_t qb = rows > 0 ? (uint32_t)(((rows - 1) * a.q_row + DQK) * 2) : 0u;
@@ -566,15 +595,15 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
         for (int i = 0; i < C::O_LOADS; ++i)
             load_lds16(ro, o_off[i], Os + slot * C::O_ELEMS + (i * kThreads + wave * 64) * 8);
-        if (tid < kQT) {
+        if (tid < kQT) {  // raw values: converted at sync time, so no wait here
             const bool ok = qt + tid < sq.sq;
-            pre_l = ok ? lse_log2(lse_h[qt + tid]) : INFINITY;
+            pre_l = ok ? lse_h[qt + tid] : -INFINITY;
             pre_d = ok ? d_h[qt + tid] : 0.f;
         }
     };
     auto sync_tiles = [&](int slot) {
         if (tid < kQT) {
-            row_lse2[slot][tid] = pre_l;
+            row_lse2[slot][tid] = lse_log2(pre_l);
             row_d[slot][tid] = pre_d;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -587,40 +616,72 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     orr.init(Os, lane);
     const float cl2 = a.scale_log2;
 
-    auto step = [&](int qt, auto slot_c) {
+    // This lane holds rows qt + 8 g + 4 half + i of a tile (element
+    // j = 4 g + i); their log2 LSE and D, four rows per load.  Plain loads
+    // (the compiler tracks their completion), issued right after the barrier
+    // and before the next tile's DMA, so they wait for no tile load.
+    auto row_values = [&](int slot, float4 (&l4)[4], float4 (&d4)[4]) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            l4[g] = *reinterpret_cast<const float4*>(&row_lse2[slot][8 * g + 4 * half]);
+            d4[g] = *reinterpret_cast<const float4*>(&row_d[slot][8 * g + 4 * half]);
+        }
+    };
+    auto step = [&](int qt, auto slot_c, float4 (&l4)[4], float4 (&d4)[4]) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int QO = slot * C::Q_ELEMS * 2, OO = slot * C::O_ELEMS * 2;  // slot byte offsets
-        f32x16 s, dp;
-        for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
-        gemm_rows1<E, DQK, QO>(qr, s, kf);  // S = Q K^T (this lane: one key, 16 rows)
-        gemm_rows1<E, DV, OO>(orr, dp, vf);  // dP = dO V^T
-        // this lane holds rows qt + 8 (j / 4) + 4 half + j % 4
+        constexpr int NBV = DV / 32, NBK = DQK / 32;
+        // complete the row-value loads before the GEMM reads are issued
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            asm volatile("" ::"v"(l4[g].x), "v"(l4[g].y), "v"(l4[g].z), "v"(l4[g].w), "v"(d4[g].x), "v"(d4[g].y),
+                         "v"(d4[g].z), "v"(d4[g].w));
+        f32x16 sa[1], dpa[1];
+        for (int j = 0; j < 16; ++j) sa[0][j] = dpa[0][j] = 0.f;
+        gemm_rows<E, DQK, 1, QO, 3>(qr, sa, kf, NoSide{});  // S = Q K^T (this lane: one key, 16 rows)
+        f32x16& s = sa[0];
         if (!(qt >= full_lo && qt + kQT - 1 <= full_hi)) {
             const uint32_t base = (uint32_t)(qt + half * 4) - q_first;
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 if (base + (uint32_t)((j >> 2) * 8 + (j & 3)) > q_span) s[j] = -INFINITY;
         }
-        // P and dS; the rows' LSE and D come four at a time
+        // dP = dO V^T; meanwhile P = exp2(S scale log2e - LSE log2e)
+        // replaces S, 16 / (D_v / 16) elements per k-step
         v8 pf[2], dsf[2];
+        gemm_rows<E, DV, 1, OO, 3>(orr, dpa, vf, [&](auto t_c) {
+            constexpr int t = decltype(t_c)::value, per = 16 / (DV / 16);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *reinterpret_cast<const float4*>(&row_lse2[slot][8 * g + 4 * half]);
-            const float4 d4 = *reinterpret_cast<const float4*>(&row_d[slot][8 * g + 4 * half]);
-            const float l2[4] = {l4.x, l4.y, l4.z, l4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * g + i;
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[j], cl2, -l2[i]));
-                pf[j >> 3][j & 7] = (T)pv;
-                dsf[j >> 3][j & 7] = (T)(pv * (dp[j] - dd[i]));
+            for (int j = t * per; j < (t + 1) * per; ++j) {
+                const float l2 = (j & 3) == 0 ? l4[j >> 2].x : (j & 3) == 1 ? l4[j >> 2].y : (j & 3) == 2 ? l4[j >> 2].z : l4[j >> 2].w;
+                s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], cl2, -l2));
+                pf[j >> 3][j & 7] = (T)s[j];
             }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 rows
-        gemm_tr_step<E, DV, OO>(orr, dv, pf[0]);
-        gemm_tr_step<E, DV, OO + 16 * DV * 2>(orr, dv, pf[1]);
-        gemm_tr_step<E, DQK, QO>(qr, dk, dsf[0]);
-        gemm_tr_step<E, DQK, QO + 16 * DQK * 2>(qr, dk, dsf[1]);
+        });
+        const f32x16& dp = dpa[0];
+        auto ds_slice = [&](int h) {
+#pragma unroll
+            for (int j = 8 * h; j < 8 * h + 8; ++j) {
+                const float dd = (j & 3) == 0 ? d4[j >> 2].x : (j & 3) == 1 ? d4[j >> 2].y : (j & 3) == 2 ? d4[j >> 2].z : d4[j >> 2].w;
+                dsf[h][j & 7] = (T)(s[j] * (dp[j] - dd));
+            }
+        };
+        // dV^T += dO^T P, then dK^T += Q^T dS over the tile's 32 rows, in
+        // steps of 16 rows; each step's transposed reads are issued before
+        // the previous step's MFMAs and dS is computed under the dV MFMAs
+        s16x4 xa[2 * NBK], xb[2 * NBK];
+        tr_issue<DV, OO>(orr, xa);
+        tr_issue<DV, OO + 16 * DV * 2>(orr, xb);
+        tr_mfma<E, DV, 2 * NBV>(xa, dv, pf[0], [&](auto c_c) {
+            if constexpr (decltype(c_c)::value == 0) ds_slice(0);
+        });
+        tr_issue<DQK, QO>(qr, xa);
+        tr_mfma<E, DV, 2 * NBK>(xb, dv, pf[1], [&](auto c_c) {
+            if constexpr (decltype(c_c)::value == 0) ds_slice(1);
+        });
+        tr_issue<DQK, QO + 16 * DQK * 2>(qr, xb);
+        tr_mfma<E, DQK, 2 * NBK>(xa, dk, dsf[0], NoSide{});
+        tr_mfma<E, DQK, 0>(xb, dk, dsf[1], NoSide{});
     };
 
     // Tiles in pairs over the two LDS slots (constant slot per step, no
@@ -630,16 +691,22 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         issue(q_lo, 0);
         sync_tiles(0);
         int i = 0;
+        float4 l4[4], d4[4];
         for (; i + 2 <= ntiles; i += 2) {
             const int qt = q_lo + i * kQT;
+            row_values(0, l4, d4);
             issue(qt + kQT, 1);
-            step(qt, std::integral_constant<int, 0>{});
+            step(qt, std::integral_constant<int, 0>{}, l4, d4);
             sync_tiles(1);
+            row_values(1, l4, d4);
             if (i + 2 < ntiles) issue(qt + 2 * kQT, 0);
-            step(qt + kQT, std::integral_constant<int, 1>{});
+            step(qt + kQT, std::integral_constant<int, 1>{}, l4, d4);
             sync_tiles(0);
         }
-        if (i < ntiles) step(q_lo + i * kQT, std::integral_constant<int, 0>{});
+        if (i < ntiles) {
+            row_values(0, l4, d4);
+            step(q_lo + i * kQT, std::integral_constant<int, 0>{}, l4, d4);
+        }
     }
 
     if (!key_ok) return;
