@@ -221,10 +221,11 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
  *   D  = rowsum(dO * O)
  *   dS = P * (dO V^T - D)
  *   dQ = softmax_scale dS K,  dK = softmax_scale dS^T Q,  dV = P^T dO
- * The dQ pass splits each query block's keys as sk_attn_partial does (blocks
- * of 128 rows, the count formula at the block's last row, split count
- * sk_split_kv(p)) and sums the split results; dK and dV are computed per
- * block of 128 keys over every row that sees one of them.
+ * The dQ pass cuts each block of 128 query rows' keys into S_dq splits with
+ * the count formula at the block's last row and sums the split results in
+ * f32; S_dq (1..8) is chosen for the current device to fill whole rounds of
+ * workgroups, and only the f32 summation order depends on it.  dK and dV are
+ * computed per block of 128 keys over every row that sees one of them.
  * Storage: dtype SK_BF16 or SK_F16 (SK_F32: SK_ERR_UNSUPPORTED), out_dtype
  * must equal dtype; head dims (64, 64), (128, 128) or (192, 128).  P and dS
  * are rounded to the storage type before their products, which accumulate in
@@ -248,8 +249,8 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
                            int64_t workspace_bytes, void* stream);
 
 /* Bytes of workspace sk_attn_backward needs for `p` on the current device
- * (f32 D per (head, row) and one f32 dQ sum per (head, split, row, dim)), or
- * -1 if `p` is invalid. */
+ * (f32 D per (head, row) and one f32 dQ sum per (head, S_dq split, row, dim);
+ * S_dq depends on the device's CU count), or -1 if `p` is invalid. */
 int64_t sk_backward_workspace_bytes(const sk_problem* p);
 
 #ifdef __cplusplus

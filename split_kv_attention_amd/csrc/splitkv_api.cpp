@@ -188,19 +188,49 @@ sk_problem resolved(const sk_problem& p) {
     return r;
 }
 
+// Split count of the backward's dQ pass.  dQ is a plain sum over key
+// splits, so the count is free: one workgroup per CU runs a 128-row block's
+// split, and S is chosen in 1..8 (at most one split per 512 keys) to
+// minimise the rounds of workgroups per unit of work, ceil(items S / CUs) / S
+// with items = query blocks x heads (smallest S on ties).  Without a device
+// (CU count unknown) it is the problem's split count.
+constexpr int kBwdQBlock = 128;
+int32_t backward_dq_splits(const sk_problem& p) {
+    const int64_t slots = cu_count();
+    if (slots <= 0) return p.split_kv;
+    int64_t blocks = (int64_t)p.batch * ((p.max_seqlen_q + kBwdQBlock - 1) / kBwdQBlock);
+    if (p.cu_seqlens_q)
+        blocks = std::min(blocks, ((int64_t)p.total_q + kBwdQBlock - 1) / kBwdQBlock + p.batch - 1);
+    const int64_t items = std::max<int64_t>(blocks, 1) * p.num_heads;
+    const int64_t max_s = std::clamp<int64_t>(p.max_seqlen_k / 512, 1, 8);
+    int32_t best = 1;
+    int64_t best_num = (items + slots - 1) / slots, best_den = 1;  // cost = num / den
+    for (int64_t s = 2; s <= max_s; ++s) {
+        const int64_t num = (items * s + slots - 1) / slots;
+        if (num * best_den < best_num * s) {
+            best = (int32_t)s;
+            best_num = num;
+            best_den = s;
+        }
+    }
+    return best;
+}
+
 // Workspace of the backward: D [H][rows] f32, then the per-split dQ sums
-// [H][S_max][rows][D_qk] f32, each 256-byte aligned.
+// [H][S_dq][rows][D_qk] f32, each 256-byte aligned.
 struct BackwardLayout {
     int64_t dvec_offset, dq_part_offset, total;
+    int32_t dq_splits;
 };
 BackwardLayout backward_layout(const sk_problem& p) {
     auto round_up = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t rows = rows_of(p);
     BackwardLayout w;
+    w.dq_splits = backward_dq_splits(p);
     w.dvec_offset = 0;
     w.dq_part_offset = round_up((int64_t)p.num_heads * rows * (int64_t)sizeof(float));
     w.total = w.dq_part_offset +
-              round_up((int64_t)p.num_heads * p.split_kv * rows * p.head_dim_qk * (int64_t)sizeof(float));
+              round_up((int64_t)p.num_heads * w.dq_splits * rows * p.head_dim_qk * (int64_t)sizeof(float));
     return w;
 }
 
@@ -435,9 +465,10 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
         if (s > ((int64_t)1 << 24)) return fail(SK_ERR_UNSUPPORTED, "row strides above 2^24 elements are not supported");
     if (p->batch > 65535 || p->num_heads > 65535)
         return fail(SK_ERR_UNSUPPORTED, "batch and num_heads above 65535 are not supported by the backward");
+    if (kern.q_block != kBwdQBlock) return fail(SK_ERR_HIP, "internal: backward query block mismatch");
     const int64_t n_qtiles = ((int64_t)p->max_seqlen_q + kern.q_block - 1) / kern.q_block;
     const int64_t n_ktiles = ((int64_t)p->max_seqlen_k + kern.k_block - 1) / kern.k_block;
-    if (n_qtiles * p->num_heads * p->split_kv * p->batch >= ((int64_t)1 << 31) ||
+    if (n_qtiles * p->num_heads * w.dq_splits * p->batch >= ((int64_t)1 << 31) ||
         n_ktiles * p->num_heads * p->batch >= ((int64_t)1 << 31) ||
         ((int64_t)p->max_seqlen_q * (p->head_dim_qk / 4) + 255) / 256 > 0x7fffffff)
         return fail(SK_ERR_UNSUPPORTED, "problem too large for the backward grids");
@@ -456,6 +487,8 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
     a.dvec = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.dvec_offset);
     a.dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.dq_part_offset);
     a.seqs = seq_table(*p);
+    a.seqs.splits = nullptr;  // the dQ pass's own uniform split count
+    a.seqs.s_max = w.dq_splits;
     a.q_row = p->q_stride_row;
     a.q_head = p->q_stride_head;
     a.q_batch = p->q_stride_batch;

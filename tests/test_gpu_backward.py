@@ -141,18 +141,31 @@ def test_backward_empty_sequences():
     assert (_f64(_rows(w, dk, 1, 1, "k")) == 0).all() and (_f64(_rows(w, dv, 1, 1, "k")) == 0).all()
 
 
-def test_backward_split_count_changes_only_rounding():
-    """dQ is a plain sum of the split sums: S = 1 and S = 5 agree to f32
-    summation order plus the final rounding."""
-    base = _shrink(workloads.LONG_PREFILL, name="bwd_split_invariance", sq=(200,), sk=(3000,), heads=2)
-    res = []
-    for S in (1, 5):
-        w = _shrink(base, split_kv=S)
+def _dq_splits(w, inputs):
+    """S_dq the library chose, read back from the workspace size."""
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], partial_scratch=False,
+                                   **workloads.problem_kwargs(w, inputs))
+    rows, H, D = prob.rows, w.heads, w.d_qk
+    first = (H * rows * 4 + 255) // 256 * 256
+    per_split = H * rows * D * 4
+    nbytes = _lib.sk_backward_workspace_bytes(prob.c)
+    assert (nbytes - first) % 256 == 0
+    return -(-(nbytes - first) // per_split) if per_split else 0
+
+
+def test_backward_dq_split_count_follows_the_device():
+    """dQ is a plain sum over key splits, so the library picks S_dq to fill
+    the GPU: several splits for one short query block with long keys, one
+    for short keys; both agree with the oracle."""
+    many = _shrink(workloads.LONG_PREFILL, name="bwd_dq_many_splits", sq=(200,), sk=(3000,), heads=2)
+    one = _shrink(workloads.CAUSAL_BF16, name="bwd_dq_one_split", sq=(300, 300), sk=(500, 500), heads=2)
+    for w, expect_many in ((many, True), (one, False)):
         inputs = workloads.make_inputs(w, DEV, 8)
-        _, _, dq, dk, dv = run_backward(w, seed=8, inputs=inputs)
-        res.append((dq.float(), dk.float(), dv.float()))
-    for a, b in zip(*res):
-        assert torch.allclose(a, b, rtol=2e-2, atol=2e-2 * float(a.abs().max()))
+        s_dq = _dq_splits(w, inputs)
+        log(f"backward {w.name}: S_dq = {s_dq}")
+        assert (s_dq > 1) if expect_many else (s_dq == 1)
+        _, dout, dq, dk, dv = run_backward(w, seed=8, inputs=inputs)
+        compare_all(w, inputs, dout, dq, dk, dv)
 
 
 def test_backward_full_size_prefill_sampled():
