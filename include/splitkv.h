@@ -77,7 +77,7 @@ typedef enum sk_dtype {
 } sk_dtype;
 
 typedef struct sk_problem {
-    int32_t batch;          /* B >= 0: number of sequences */
+    int32_t batch;          /* 0 <= B <= 65535: number of sequences */
     int32_t num_heads;      /* H >= 1 (query, key and value heads are equal) */
     int32_t max_seqlen_q;   /* dense: every Sq_b; varlen: >= every Sq_b */
     int32_t max_seqlen_k;   /* dense: every Sk_b; varlen: >= every Sk_b */

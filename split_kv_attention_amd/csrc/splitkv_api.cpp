@@ -51,6 +51,8 @@ const char* dtype_name(int dtype) { return dtype == SK_BF16 ? "bf16" : dtype == 
 sk_status check_problem(const sk_problem* p) {
     if (!p) return fail(SK_ERR_INVALID_ARG, "problem is NULL");
     if (p->batch < 0) return fail(SK_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", p->batch);
+    // counts (and the packed combine) take one grid row per sequence
+    if (p->batch > 65535) return fail(SK_ERR_UNSUPPORTED, "batch above 65535 is not supported (got %d)", p->batch);
     if (p->num_heads < 1) return fail(SK_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", p->num_heads);
     if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
         return fail(SK_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0 (got %d, %d)", p->max_seqlen_q, p->max_seqlen_k);
@@ -463,8 +465,7 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
     const int64_t row_strides[] = {p->q_stride_row, p->k_stride_row, p->v_stride_row, p->o_stride_row};
     for (int64_t s : row_strides)
         if (s > ((int64_t)1 << 24)) return fail(SK_ERR_UNSUPPORTED, "row strides above 2^24 elements are not supported");
-    if (p->batch > 65535 || p->num_heads > 65535)
-        return fail(SK_ERR_UNSUPPORTED, "batch and num_heads above 65535 are not supported by the backward");
+    if (p->num_heads > 65535) return fail(SK_ERR_UNSUPPORTED, "num_heads above 65535 is not supported by the backward");
     if (kern.q_block != kBwdQBlock) return fail(SK_ERR_HIP, "internal: backward query block mismatch");
     const int64_t n_qtiles = ((int64_t)p->max_seqlen_q + kern.q_block - 1) / kern.q_block;
     const int64_t n_ktiles = ((int64_t)p->max_seqlen_k + kern.k_block - 1) / kern.k_block;

@@ -100,6 +100,7 @@ def _all_calls(p):
 BAD = [
     ("num_heads", 0, sk.SK_ERR_INVALID_ARG),
     ("batch", -1, sk.SK_ERR_INVALID_ARG),
+    ("batch", 65536, sk.SK_ERR_UNSUPPORTED),
     ("max_seqlen_q", -5, sk.SK_ERR_INVALID_ARG),
     ("split_kv", -1, sk.SK_ERR_INVALID_ARG),
     ("split_kv", 1000, sk.SK_ERR_UNSUPPORTED),
