@@ -15,8 +15,9 @@
 //    forward's layout (4 waves, 32 query rows each, one query per lane):
 //    S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q^T and dO^T in
 //    registers), dS^T in registers as the B operand of dQ^T += K^T dS^T (K
-//    read transposed from LDS).  The key range is the forward's split of the
-//    block, so a long key axis runs as many workgroups; each writes its dQ
+//    read transposed from LDS).  The block's keys are cut into S_dq splits by
+//    the count formula at its last row (S_dq chosen by the host to fill the
+//    GPU), so a long key axis runs as many workgroups; each writes its dQ
 //    sum to a workspace.
 //  * bwd_dkdv: per (sequence, head, block of 128 keys), the same layout with
 //    keys and queries swapped (one key per lane): S = Q K^T and dP = dO V^T
