@@ -36,3 +36,37 @@ def test_the_check_flags_a_copy_before_the_wait():
     assert violations(ok) == []
     late = ["ds_read_b128 v[0:3], v92", "ds_read_b128 v[4:7], v93", "s_waitcnt lgkmcnt(1)", "v_mov_b32_e32 v9, v4"]
     assert len(violations(late)) == 1
+
+
+def test_the_check_follows_branches_and_loops():
+    """Planted mistakes that a straight walk would miss: a use on the taken
+    side of a branch whose fall-through side waits, and a read at the end of
+    a loop body used at its head through the back edge."""
+    branch = [
+        "ds_read_b128 v[0:3], v92",
+        "s_cbranch_scc1 .LBB0_2",
+        "s_waitcnt lgkmcnt(0)",
+        "v_mov_b32_e32 v5, v0",
+        "s_branch .LBB0_3",
+        ".LBB0_2:",
+        "v_mov_b32_e32 v6, v1",
+        ".LBB0_3:",
+        "s_waitcnt lgkmcnt(0)",
+        "v_mov_b32_e32 v7, v2",
+    ]
+    v = violations(branch)
+    assert len(v) == 1 and "v6" in v[0], v
+    loop = [
+        "s_mov_b32 s0, 0",
+        ".LBB1_1:",
+        "v_add_f32_e32 v8, v8, v4",
+        "ds_read_b128 v[4:7], v93",
+        "s_add_i32 s0, s0, 1",
+        "s_cmp_lt_i32 s0, 8",
+        "s_cbranch_scc1 .LBB1_1",
+        "s_waitcnt lgkmcnt(0)",
+    ]
+    v = violations(loop)
+    assert len(v) == 1 and "v4" in v[0], v
+    loop_ok = loop[:4] + ["s_waitcnt lgkmcnt(0)"] + loop[4:]
+    assert violations(loop_ok) == []
