@@ -93,7 +93,8 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
 
 def time_backward(w, prob, inputs, out, lse, stream, steps: int):
     """sk_attn_backward on the forward's out / LSE and a seeded dO, timed
-    with HIP events on `stream` over `steps` calls after 2 warmup calls.
+    with HIP events on `stream` over `steps` calls after 3 warmup calls
+    (the forward's warm-up has already brought the clock up).
 
     FLOPs: the five products of attention's gradient over the Sq x Sk pairs
     (recomputed scores Q K^T and dO V^T, dV = P^T dO, dQ = dS K,
@@ -114,7 +115,7 @@ def time_backward(w, prob, inputs, out, lse, stream, steps: int):
     def call():
         _lib.sk_attn_backward(prob.c, q, k, v, out, dout, lse, dq, dk, dv, ws, nbytes, sh)
 
-    for _ in range(2):
+    for _ in range(3):
         call()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -146,8 +147,11 @@ def time_backward(w, prob, inputs, out, lse, stream, steps: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The shader clock takes tens of milliseconds to settle under this load:
+    # 50 untimed steps (~60 ms) before the 100 timed ones (5 left the step
+    # ~2% slower).
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10, help="combine timings after a cache flush")
     ap.add_argument("--backward-steps", type=int, default=10, help="timed backward calls (0: skip)")
