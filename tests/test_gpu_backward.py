@@ -190,6 +190,32 @@ def test_backward_full_size_prefill_sampled():
         log(f"  head {h}: {st}")
 
 
+def test_backward_full_size_packed_batch_sampled():
+    """The packed 4-sequence batch (Sq = 4096 each, Sk = 8K / 32K / 64K /
+    128K, prefix-causal with the query rows at the end of the keys) at full
+    size: dQ at sampled rows and dK, dV at sampled keys of the shortest and
+    the longest sequence against the oracle's chunked gradients."""
+    w = workloads.VARLEN_BATCH_PREFIX
+    log(f"backward full {w.name}")
+    inputs, dout, dq, dk, dv = run_backward(w, seed=4)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    q0 = [0] + list(np.cumsum(w.sq)[:-1])
+    k0 = [0] + list(np.cumsum(w.sk)[:-1])
+    for b, h in ((0, 0), (3, 5)):
+        rows = sample_rows(w.sq[b], 12, 10 + b, 128)
+        keys = sample_rows(w.sk[b], 12, 20 + b, 128)
+        # keys that only the last rows see, and the very last ones
+        keys = np.unique(np.concatenate([keys, [w.sk[b] - 4096, w.sk[b] - 4095, w.sk[b] - 2, w.sk[b] - 1]]))
+        rq, rk, rv = adapter.backward_sampled(w, inputs, dout, b, h, rows, keys)
+        st = [
+            _check("dQ", _f64(dq[torch.as_tensor(q0[b] + rows, device=DEV), h]), rq),
+            _check("dK", _f64(dk[torch.as_tensor(k0[b] + keys, device=DEV), h]), rk),
+            _check("dV", _f64(dv[torch.as_tensor(k0[b] + keys, device=DEV), h]), rv),
+        ]
+        log(f"  sequence {b} head {h}: {st}")
+
+
 def test_backward_rejects_f32_and_mismatched_out_dtype():
     w = _shrink(workloads.TINY_F32, name="bwd_f32")
     inputs = workloads.make_inputs(w, DEV, 0)
