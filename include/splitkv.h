@@ -239,7 +239,8 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
  *              written (keys no row sees get 0); rows of a packed K/V that
  *              belong to no sequence are left untouched
  *   workspace  device memory of at least sk_backward_workspace_bytes(p)
- *              bytes, 16-byte aligned; contents on entry do not matter
+ *              bytes, 16-byte aligned; contents on entry do not matter; it
+ *              may not be shared by calls that can run at the same time
  * Every tensor must be 16-byte aligned with strides that are multiples of 8
  * elements, and the row strides of q, k, v and the outputs must not exceed
  * 2^24 elements.  The result does not depend on split_kv beyond f32
