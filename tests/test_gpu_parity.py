@@ -294,6 +294,41 @@ def test_small_cases_all_rows(w):
     log(f"  {st}")
 
 
+def test_maximum_split_count():
+    """split_kv = 128, the most the library takes, at a key tile of 1: the
+    combine merges each row in four chunks of 32 splits, and most splits of
+    the early rows are empty."""
+    w = _shrink(workloads.CAUSAL_BF16, name="max_splits_S128", heads=2, n_per_block=1, split_kv=128, sq=(150, 150),
+                sk=(300, 300), mask="prefix_causal", prefix_offset=150)
+    log(f"e2e {w.name}")
+    inputs, prob, res = run_gpu(w, seed=6)
+    st = compare(w, inputs, prob, res, label=w.name)
+    log(f"  {st}")
+    assert int(res["counts"].max()) == 128
+
+
+def test_maximum_batch_packed():
+    """65535 packed sequences, the most the library takes (one grid row of
+    the combine per sequence), with ragged lengths of 0..3 rows and 0..40
+    keys, bottom-right prefix-causal offsets and two splits; compared on a
+    sample of sequences, and the output is finite everywhere."""
+    B = 65535
+    rng = np.random.default_rng(65535)
+    sq = tuple(int(x) for x in rng.integers(0, 4, B))
+    sk = tuple(int(x) for x in rng.integers(0, 41, B))
+    w = Workload("max_batch_B65535", heads=1, sq=sq, sk=sk, d_qk=64, d_v=64, split_kv=2, n_per_block=8,
+                 mask="prefix_causal", packed=True, prefix_offset_per_seq=tuple(k - q for q, k in zip(sq, sk)))
+    log(f"e2e {w.name}")
+    inputs, prob, res = run_gpu(w, seed=7)
+    picked = set([0, 1, B - 2, B - 1] + [int(x) for x in rng.choice(B, 300, replace=False)])
+    rows_per_seq = {b: (np.arange(sq[b]) if b in picked else np.array([], dtype=np.int64)) for b in range(B)}
+    st = compare(w, inputs, prob, res, rows_per_seq=rows_per_seq, label=w.name)
+    log(f"  {st}")
+    assert torch.isfinite(res["out"]).all()
+    del inputs, res
+    torch.cuda.empty_cache()
+
+
 def test_empty_sequences_in_a_packed_batch():
     """Sk = 0 gives zero output / -inf LSE without error; Sq = 0 is skipped."""
     w = _shrink(workloads.VARLEN_BATCH, name="empties", sq=(5, 0, 40, 3), sk=(0, 100, 0, 90),
