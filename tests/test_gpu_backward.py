@@ -216,6 +216,39 @@ def test_backward_full_size_packed_batch_sampled():
         log(f"  sequence {b} head {h}: {st}")
 
 
+def test_backward_maximum_batch_packed():
+    """65535 packed sequences (the most the library takes) of 0..3 rows and
+    0..40 keys, bottom-right prefix-causal: every gradient finite, and the
+    gradients of 300 sampled sequences (all their rows and keys) against the
+    oracle."""
+    B = 65535
+    rng = np.random.default_rng(65536)
+    sq = tuple(int(x) for x in rng.integers(0, 4, B))
+    sk = tuple(int(x) for x in rng.integers(0, 41, B))
+    w = workloads.Workload("bwd_max_batch_B65535", heads=1, sq=sq, sk=sk, d_qk=64, d_v=64, split_kv=2,
+                           n_per_block=8, mask="prefix_causal", packed=True,
+                           prefix_offset_per_seq=tuple(k - q for q, k in zip(sq, sk)))
+    log(f"backward {w.name}")
+    inputs, dout, dq, dk, dv = run_backward(w, seed=8)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    q0 = np.concatenate([[0], np.cumsum(sq)[:-1]])
+    k0 = np.concatenate([[0], np.cumsum(sk)[:-1]])
+    got = {"dQ": [], "dK": [], "dV": []}
+    ref = {"dQ": [], "dK": [], "dV": []}
+    dq_c, dk_c, dv_c = _f64(dq[:, 0]), _f64(dk[:, 0]), _f64(dv[:, 0])
+    for b in sorted(set([0, 1, B - 2, B - 1] + [int(x) for x in rng.choice(B, 300, replace=False)])):
+        rq, rk, rv = adapter.backward_sampled(w, inputs, dout, b, 0, np.arange(sq[b]), np.arange(sk[b]))
+        got["dQ"].append(dq_c[q0[b] : q0[b] + sq[b]].ravel())
+        got["dK"].append(dk_c[k0[b] : k0[b] + sk[b]].ravel())
+        got["dV"].append(dv_c[k0[b] : k0[b] + sk[b]].ravel())
+        ref["dQ"].append(rq.ravel())
+        ref["dK"].append(rk.ravel())
+        ref["dV"].append(rv.ravel())
+    st = {n: _check(n, np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    log(f"  {st}")
+
+
 def test_backward_rejects_f32_and_mismatched_out_dtype():
     w = _shrink(workloads.TINY_F32, name="bwd_f32")
     inputs = workloads.make_inputs(w, DEV, 0)
