@@ -74,12 +74,14 @@ def _half_ulp(x: np.ndarray, mantissa_bits: int) -> np.ndarray:
     return np.where(ax > 0, np.exp2(e - mantissa_bits - 1), 0.0)
 
 
-def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=True, label=""):
-    """Compare GPU results with the oracle on the listed rows; returns stats."""
+def compare(w, inputs, prob, res, rows_per_seq=None, heads=None, check_partials=True, label="", exp=None):
+    """Compare GPU results with the oracle on the listed rows; returns stats.
+    `exp`: the oracle's results (adapter.expected) when already computed."""
     f32_in = w.dtype == "f32"
     tol = TOL_F32 if f32_in else TOL_BF16
     mpb = prob.m_per_block
-    exp = adapter.expected(w, inputs, mpb, rows_per_seq=rows_per_seq, heads=heads)
+    if exp is None:
+        exp = adapter.expected(w, inputs, mpb, rows_per_seq=rows_per_seq, heads=heads)
     starts = adapter.row_starts(w)
     specs = adapter.seq_specs(w)
     gc = res["counts"].cpu().numpy()

@@ -1,7 +1,9 @@
 """GPU parity: libsplitkv (through its C ABI) against the float64 oracle.
 
 Small cases are compared on every row; the full-size workloads, in the launch
-configuration the benchmark times, on sampled rows / (sequence, head) pairs.
+configuration the benchmark times, on every row and head (long-context
+prefill, prefix-causal packed batch) or on sampled rows / (sequence, head)
+pairs.
 """
 import dataclasses
 import json
@@ -435,6 +437,25 @@ def test_full_prefill_sampled_rows(w):
     # every written slot is finite or -inf; the output has no NaN anywhere
     assert torch.isfinite(res["out"]).all()
     del inputs, res
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", [workloads.LONG_PREFILL, workloads.VARLEN_BATCH_PREFIX], ids=lambda w: w.name)
+def test_full_prefill_every_row_and_head(w):
+    """The long-context prefill (H = 12, Sq = 4096, Sk = 42700, split 3) and
+    the prefix-causal packed batch (4 x Sq = 4096, Sk 8K..128K, splits 2..8)
+    at full size on every row of every head: counts, partials and the merged
+    output and LSE against the oracle (about 1 s of host time per head for
+    the prefill, five times that for the batch)."""
+    log(f"full {w.name}, every row and head")
+    inputs, prob, res = run_gpu(w)
+    host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inputs.items()}
+    stats = []
+    for h in range(w.heads):
+        exp = adapter.expected(w, host, prob.m_per_block, heads=[h])
+        stats.append(compare(w, inputs, prob, res, heads=[h], label=f"{w.name} h={h}", exp=exp))
+        log(f"  head {h}: {stats[-1]}")
+    del inputs, res, host
     torch.cuda.empty_cache()
 
 
