@@ -190,6 +190,26 @@ def test_backward_full_size_prefill_sampled():
         log(f"  head {h}: {st}")
 
 
+def test_backward_full_size_prefill_every_row_and_key():
+    """The long-context prefill at full size: dQ at every row and dK, dV at
+    every key of every head against the oracle's chunked gradients (about
+    3 s of host time per head)."""
+    w = workloads.LONG_PREFILL
+    log(f"backward full {w.name}, every row, key and head")
+    inputs, dout, dq, dk, dv = run_backward(w, seed=5)
+    host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inputs.items()}
+    dout_h = dout.cpu()
+    rows, keys = np.arange(w.sq[0]), np.arange(w.sk[0])
+    for h in range(w.heads):
+        rq, rk, rv = adapter.backward_sampled(w, host, dout_h, 0, h, rows, keys)
+        st = [
+            _check("dQ", _f64(dq[:, h]), rq),
+            _check("dK", _f64(dk[:, h]), rk),
+            _check("dV", _f64(dv[:, h]), rv),
+        ]
+        log(f"  head {h}: {st}")
+
+
 def test_backward_full_size_packed_batch_sampled():
     """The packed 4-sequence batch (Sq = 4096 each, Sk = 8K / 32K / 64K /
     128K, prefix-causal with the query rows at the end of the keys) at full
