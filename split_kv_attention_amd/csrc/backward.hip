@@ -273,7 +273,7 @@ void bwd_dq_kernel(BackwardArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int qrow = r0 + wave * 32 + col;
-    const bool row_ok = qrow < sq.sq;
+    const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
     const int64_t prow = sq.row0 + qrow;
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
     const int lo_q = (int)min(vis_first(sq, win, qrow), (int64_t)0x7fffffff);

@@ -125,7 +125,7 @@ void partial_bf16_kernel(PartialArgs a) {
     const int col = lane & 31;   // query column of this lane (and A-row for loads)
     const int half = lane >> 5;  // which 8-wide k slice / which 4 accumulator rows
     const int qrow = r0 + wave * 32 + col;
-    const bool row_ok = qrow < sq.sq;
+    const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
     const bool wave_active = (r0 + wave * 32) < sq.sq;
     // Visibility limits of this lane's row, clamped into int range (keys are int).
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
 
     const int lane = threadIdx.x;
     const int qrow = r0 + lane;
-    const bool row_ok = qrow < sq.sq;
+    const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
     const int64_t vis = vis_last(sq, mask, qrow);
     const int64_t lo = vis_first(sq, win, qrow);
 

@@ -258,6 +258,7 @@ BackwardKernel find_backward(int dtype, int d_qk, int d_v);
 struct CountsArgs {
     int32_t* counts;
     SeqTable seqs;
+    int64_t rows;  // length of counts: rows past it (inconsistent cu_seqlens) are not written
 };
 
 struct CombineArgs {

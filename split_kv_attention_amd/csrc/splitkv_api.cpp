@@ -311,6 +311,7 @@ sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stre
     sk::CountsArgs a;
     a.counts = counts;
     a.seqs = seq_table(*p);
+    a.rows = rows_of(*p);
     return hip_status(sk::launch_counts(a, p->batch, (hipStream_t)stream), "counts kernel launch");
 }
 
