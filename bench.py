@@ -42,9 +42,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(launch_units: float):
-    """HBM bytes per launch of the partial kernel from the committed rocprofv3
-    counter summary, or None when absent or taken on different kernel code."""
+def measured_traffic():
+    """HBM bytes per launch of the partial entry point from the committed
+    rocprofv3 counter summary, or None when absent or taken on different
+    kernel code."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -55,10 +56,11 @@ def measured_traffic(launch_units: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inputs, budget_s: float = 12.0):
+def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 12.0):
     """The oracle (as it stands) on a bounded sample of the same workload:
-    the full split method (counts, partials, merge) for chunks of query rows
-    over all heads and all 42700 keys, until `budget_s` of wall time."""
+    the full split method (counts, partials at the kernel's query block,
+    merge) for chunks of query rows over all heads and all 42700 keys, until
+    `budget_s` of wall time."""
     import numpy as np
 
     from oracle import adapter
@@ -77,7 +79,7 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
     t0 = time.perf_counter()
     while done < len(order) and time.perf_counter() - t0 < budget_s:
         rows = np.sort(order[done : done + chunk])
-        adapter.expected(w, host, 128, rows_per_seq={0: rows})
+        adapter.expected(w, host, m_per_block, rows_per_seq={0: rows})
         done += len(rows)
     dt = time.perf_counter() - t0
     flops = 2.0 * (w.d_qk + w.d_v) * w.heads * done * w.sk[0]
@@ -241,7 +243,7 @@ def main() -> int:
     combine_bytes = (S * H * rows * w.d_v * 4 + S * H * rows * 4 + rows * 4 + rows * H * w.d_v * 2 + H * rows * 4)
     partial_bytes = (rows * H * w.d_qk * 2 + Sk * H * (w.d_qk + w.d_v) * 2 + S * H * rows * (w.d_v + 1) * 4)
     achieved = flops / (t_partial * 1e-3) / 1e12
-    traffic = measured_traffic(1)
+    traffic = measured_traffic()
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -290,7 +292,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inputs)
+        res["cpu_baseline"] = cpu_baseline(w, inputs, prob.m_per_block)
     print(json.dumps(res), flush=True)
     return 0
 
