@@ -60,6 +60,7 @@ struct Cfg {
     static constexpr int VG = (VCH / 4) < 4 ? (VCH / 4) : 4;  // V swizzle period (rows)
     static_assert(DQK % 64 == 0 && DV % 32 == 0, "head dims must be multiples of 64 (QK) and 32 (V)");
     static_assert((kBN * KCH) % kThreads == 0 && (kBN * VCH) % kThreads == 0, "whole loads per thread");
+    static_assert(K_LOADS + V_LOADS <= DQK / 16, "one tile load per GEMM0 step");
 };
 
 // Growth of the running max (in log2 units) tolerated before the output
@@ -179,7 +180,7 @@ void partial_bf16_kernel(PartialArgs a) {
         v_off[i] = (uint32_t)(r * a.v_row + v_swz<C::VG>(r, P % C::VCH) * 8) * 2u;
     }
     // LDS: K tiles in two slots, V tiles in two slots.  K runs one tile ahead
-    // of V: while tile t is in its softmax and GEMM1, GEMM0 of tile t + 1
+    // of V: between tile t's softmax and its GEMM1, GEMM0 of tile t + 1
     // reads the other K slot.
     uint16_t* const Ks0 = smem;
     uint16_t* const Vs0 = smem + 2 * C::K_ELEMS;
@@ -209,6 +210,26 @@ void partial_bf16_kernel(PartialArgs a) {
         uint16_t* dst = Vs0 + slot * C::V_ELEMS;
 #pragma unroll
         for (int i = 0; i < C::V_LOADS; ++i) load_lds16(r, v_off[i], dst + (i * kThreads + wave * 64) * 8);
+    };
+    // The same loads, one at a time: the buffer resources of a K and a V
+    // tile, then load i of the pair (K loads first), so that the loads of a
+    // tile can be spread over the steps of a GEMM.
+    auto rsrc_k = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(k_src, kt + kBN <= ke ? k_full : tile_bytes(kt, a.k_row, DQK));
+        k_src += k_step;
+        return r;
+    };
+    auto rsrc_v = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(v_src, kt + kBN <= ke ? v_full : tile_bytes(kt, a.v_row, DV));
+        v_src += v_step;
+        return r;
+    };
+    auto issue_one = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int kslot, int vslot, auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < C::K_LOADS)
+            load_lds16(rk, k_off[i], Ks0 + kslot * C::K_ELEMS + (i * kThreads + wave * 64) * 8);
+        else if constexpr (i < C::K_LOADS + C::V_LOADS)
+            load_lds16(rv, v_off[i - C::K_LOADS], Vs0 + vslot * C::V_ELEMS + ((i - C::K_LOADS) * kThreads + wave * 64) * 8);
     };
     auto sync_tiles = [&]() {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads landed
@@ -355,36 +376,6 @@ void partial_bf16_kernel(PartialArgs a) {
                 for (int j = 0; j < 8; j += 2)
                     rs = E::dot2(bf16x2{pf[kb][u][j], pf[kb][u][j + 1]}, ones, rs);
     };
-    // The same, a slice of 2E elements at a time (E pairs), to be spread
-    // over the steps of the next tile's GEMM0.
-    constexpr int kSteps = DQK / 16;
-    constexpr int kPairsPerStep = (16 + kSteps - 1) / kSteps;
-    auto weights_slice = [&](const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float mc_in, float& rs, auto step_c) {
-        constexpr int step = decltype(step_c)::value;
-        const bf16x2 ones = {(T)1.0f, (T)1.0f};
-        if constexpr (step * kPairsPerStep < 16) {
-            const float mc = mc_in;
-#pragma unroll
-            for (int q = 0; q < kPairsPerStep; ++q) {
-                const int pr = step * kPairsPerStep + q;  // pair index 0..15
-                if (pr < 16) {
-                    const int e = 2 * pr;  // element 0..31 = 16 kb + j
-                    const int kb = e >> 4, j = e & 15;
-                    float x0 = fmaf(sacc[kb][j], cl2, -mc), x1 = fmaf(sacc[kb][j + 1], cl2, -mc);
-                    asm volatile("" : "+v"(x0), "+v"(x1));  // keeps this slice below the step's wait
-                    bf16x2 p2;
-                    p2[0] = (T)__builtin_amdgcn_exp2f(x0);
-                    p2[1] = (T)__builtin_amdgcn_exp2f(x1);
-                    uint32_t packed = __builtin_bit_cast(uint32_t, p2);
-                    asm volatile("" : "+v"(packed));  // keeps it above the next step's reads
-                    p2 = __builtin_bit_cast(bf16x2, packed);
-                    pf[kb][j >> 3][j & 7] = p2[0];
-                    pf[kb][j >> 3][(j & 7) + 1] = p2[1];
-                    rs = E::dot2(p2, ones, rs);
-                }
-            }
-        }
-    };
     // Range check of weights computed without the max update (see prepare).
     auto check_weights = [&](bool max_taken, const f32x16(&sacc)[2], bf16x8(&pf)[2][2], float& rs) {
         if (!max_taken && __builtin_amdgcn_ballot_w64(!(rs <= 0x1p64f))) {
@@ -439,9 +430,10 @@ void partial_bf16_kernel(PartialArgs a) {
         mma_step(xb, pf[1][1]);
     };
 
-    // Pipeline.  Iteration i: DMA K(i+2) -> K slot i%2 and V(i+1) -> V slot
-    // (i+1)%2; GEMM0(i+1) from K slot (i+1)%2 together with the weights of
-    // tile i; GEMM1(i) from V slot i%2; then tile i+1's mask / max update.
+    // Pipeline.  Iteration i: the weights of tile i from its scores; GEMM0(i+1)
+    // from K slot (i+1)%2 into the same score registers, with the DMA of
+    // K(i+2) -> K slot i%2 and V(i+1) -> V slot (i+1)%2 spread over its steps;
+    // GEMM1(i) from V slot i%2; then tile i+1's mask / max update.
     const int ntiles = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
     if (ntiles > 0) {
         issue_k(ks, 0);
@@ -457,19 +449,25 @@ void partial_bf16_kernel(PartialArgs a) {
         sync_tiles();
         for (int i = 0; i + 1 < ntiles; ++i) {
             const int kt = ks + i * kBN;
-            issue_k(kt + 2 * kBN, i & 1);
-            issue_v(kt + kBN, (i + 1) & 1);
+            // K(i + 2) and V(i + 1), one load per GEMM0 step: issued as one
+            // burst, the loads of a CU's 8 waves queue in its memory pipeline
+            // and hold each wave before its first MFMA.
+            const __amdgpu_buffer_rsrc_t rk = rsrc_k(kt + 2 * kBN);
+            const __amdgpu_buffer_rsrc_t rv = rsrc_v(kt + kBN);
             if (wave_active) {
-                f32x16 sn[2];
                 bf16x8 pf[2][2];
                 float rs = 0.f;
-                const float mc = (m_i == -INFINITY) ? 0.f : m_i * cl2;
-                gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sn, [&](auto step_c) { weights_slice(sc, pf, mc, rs, step_c); });
+                weights(sc, pf, rs);
                 check_weights(sc_max, sc, pf, rs);
+                gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sc, [&](auto step_c) {
+                    issue_one(rk, rv, i & 1, (i + 1) & 1, step_c);
+                });
                 gemm1(Vs0 + (i & 1) * C::V_ELEMS, pf);
-                sc_max = prepare(kt + kBN, sn);
-                sc[0] = sn[0];
-                sc[1] = sn[1];
+                sc_max = prepare(kt + kBN, sc);
+            } else {
+                [&]<int... L>(std::integer_sequence<int, L...>) {
+                    (issue_one(rk, rv, i & 1, (i + 1) & 1, std::integral_constant<int, L>{}), ...);
+                }(std::make_integer_sequence<int, C::K_LOADS + C::V_LOADS>{});
             }
             sync_tiles();
         }
