@@ -321,19 +321,32 @@ void bwd_dq_kernel(BackwardArgs a) {
     }
     uint16_t* const Ks = smem;
     uint16_t* const Vs = smem + 2 * C::K_ELEMS;
-    auto issue = [&](int kt, int slot) {
+    // Buffer resources of the K and V tile at key kt (a tile at or past the
+    // end has an empty range and loads zeros), and load i of the pair, K
+    // loads first.  The loop issues a tile's loads one per k-step of the
+    // previous tile's first GEMM: issued as one burst, they would hold the
+    // wave before its first MFMA.
+    struct TileRsrc {
+        __amdgpu_buffer_rsrc_t k, v;
+    };
+    auto rsrc = [&](int kt) {
         const int rows = min(ke - kt, kKT);
         const uint32_t kb = rows > 0 ? (uint32_t)(((rows - 1) * a.k_row + DQK) * 2) : 0u;
         const uint32_t vb = rows > 0 ? (uint32_t)(((rows - 1) * a.v_row + DV) * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + (int64_t)kt * a.k_row, kb);
-        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + (int64_t)kt * a.v_row, vb);
-#pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i)
-            load_lds16(rk, k_off[i], Ks + slot * C::K_ELEMS + (i * kThreads + wave * 64) * 8);
-#pragma unroll
-        for (int i = 0; i < C::V_LOADS; ++i)
-            load_lds16(rv, v_off[i], Vs + slot * C::V_ELEMS + (i * kThreads + wave * 64) * 8);
+        return TileRsrc{tile_rsrc(kbase + (int64_t)kt * a.k_row, kb), tile_rsrc(vbase + (int64_t)kt * a.v_row, vb)};
     };
+    auto load_one = [&](const TileRsrc& r, int slot, auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < C::K_LOADS)
+            load_lds16(r.k, k_off[i], Ks + slot * C::K_ELEMS + (i * kThreads + wave * 64) * 8);
+        else if constexpr (i < C::K_LOADS + C::V_LOADS)
+            load_lds16(r.v, v_off[i - C::K_LOADS], Vs + slot * C::V_ELEMS + ((i - C::K_LOADS) * kThreads + wave * 64) * 8);
+    };
+    auto issue = [&](int kt, int slot) {
+        const TileRsrc r = rsrc(kt);
+        static_for<C::K_LOADS + C::V_LOADS>([&](auto i_c) { load_one(r, slot, i_c); });
+    };
+    static_assert(C::K_LOADS + C::V_LOADS <= DQK / 16, "one tile load per k-step of S^T = K Q^T");
     auto sync_tiles = [&]() {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
@@ -351,7 +364,8 @@ void bwd_dq_kernel(BackwardArgs a) {
     const int full_start = lo_last <= ks ? ks : (int)min((int64_t)ke, ks + ceil_div64(lo_last - ks, kKT) * kKT);
     const float cl2 = a.scale_log2;
 
-    auto step = [&](int kt, auto slot_c) {
+    // One tile; loads(t) issues load t of the next tile into the other slot
+    auto step = [&](int kt, auto slot_c, auto&& loads) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int KO = slot * C::K_ELEMS * 2, VO = slot * C::V_ELEMS * 2;  // slot byte offsets
         constexpr int NB = DQK / 32;
@@ -359,7 +373,7 @@ void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
-        gemm_rows<E, DQK, 2, KO, 3>(kr, s, qf, NoSide{});  // S^T = K Q^T
+        gemm_rows<E, DQK, 2, KO, 3>(kr, s, qf, loads);  // S^T = K Q^T
         if (kt >= full_end || kt < full_start) {
             const int lim = min(ke - 1, vis_q) - kt - half * 4, first = lo_q - kt - half * 4;
 #pragma unroll
@@ -416,14 +430,15 @@ void bwd_dq_kernel(BackwardArgs a) {
         int i = 0;
         for (; i + 2 <= ntiles; i += 2) {
             const int kt = ks + i * kKT;
-            issue(kt + kKT, 1);
-            step(kt, std::integral_constant<int, 0>{});
+            const TileRsrc r1 = rsrc(kt + kKT);
+            step(kt, std::integral_constant<int, 0>{}, [&](auto t_c) { load_one(r1, 1, t_c); });
             sync_tiles();
-            if (i + 2 < ntiles) issue(kt + 2 * kKT, 0);
-            step(kt + kKT, std::integral_constant<int, 1>{});
+            // past the last tile the range is empty (into a slot no step reads)
+            const TileRsrc r0 = rsrc(kt + 2 * kKT);
+            step(kt + kKT, std::integral_constant<int, 1>{}, [&](auto t_c) { load_one(r0, 0, t_c); });
             sync_tiles();
         }
-        if (i < ntiles) step(ks + i * kKT, std::integral_constant<int, 0>{});
+        if (i < ntiles) step(ks + i * kKT, std::integral_constant<int, 0>{}, NoSide{});
     }
 
     if (!row_ok || prow >= a.rows) return;
@@ -584,18 +599,30 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     const float* lse_h = a.lse + (int64_t)head * a.rows + sq.row0;
     const float* d_h = a.dvec + (int64_t)head * a.rows + sq.row0;
     float pre_l = -INFINITY, pre_d = 0.f;  // this thread's row values of the next tile (threads 0..31)
-    auto issue = [&](int qt, int slot) {
+    // Buffer resources of the Q and dO tile at row qt (a tile at or past the
+    // end has an empty range and loads zeros), and load i of the pair, Q
+    // loads first.  The loop issues a tile's loads one per k-step of the
+    // previous tile's first GEMM: issued as one burst, they would hold the
+    // wave before its first MFMA.
+    struct TileRsrc {
+        __amdgpu_buffer_rsrc_t q, o;
+    };
+    auto rsrc = [&](int qt) {
         const int rows = min(sq.sq - qt, kQT);
         const uint32_t qb = rows > 0 ? (uint32_t)(((rows - 1) * a.q_row + DQK) * 2) : 0u;
         const uint32_t ob = rows > 0 ? (uint32_t)(((rows - 1) * a.o_row + DV) * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qbase + (int64_t)qt * a.q_row, qb);
-        const __amdgpu_buffer_rsrc_t ro = tile_rsrc(obase + (int64_t)qt * a.o_row, ob);
-#pragma unroll
-        for (int i = 0; i < C::Q_LOADS; ++i)
-            load_lds16(rq, q_off[i], Qs + slot * C::Q_ELEMS + (i * kThreads + wave * 64) * 8);
-#pragma unroll
-        for (int i = 0; i < C::O_LOADS; ++i)
-            load_lds16(ro, o_off[i], Os + slot * C::O_ELEMS + (i * kThreads + wave * 64) * 8);
+        return TileRsrc{tile_rsrc(qbase + (int64_t)qt * a.q_row, qb), tile_rsrc(obase + (int64_t)qt * a.o_row, ob)};
+    };
+    auto load_one = [&](const TileRsrc& r, int slot, auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < C::Q_LOADS)
+            load_lds16(r.q, q_off[i], Qs + slot * C::Q_ELEMS + (i * kThreads + wave * 64) * 8);
+        else if constexpr (i < C::Q_LOADS + C::O_LOADS)
+            load_lds16(r.o, o_off[i - C::Q_LOADS], Os + slot * C::O_ELEMS + ((i - C::Q_LOADS) * kThreads + wave * 64) * 8);
+    };
+    static_assert(C::Q_LOADS + C::O_LOADS <= DQK / 16, "one tile load per k-step of S = Q K^T");
+    // the rows' LSE and D of the tile at qt (threads 0 .. kQT - 1)
+    auto issue_rows = [&](int qt) {
         if (tid < kQT) {  // raw values: converted at sync time, so no wait here
             const bool ok = qt + tid < sq.sq;
             pre_l = ok ? lse_h[qt + tid] : -INFINITY;
@@ -628,7 +655,8 @@ void bwd_dkdv_kernel(BackwardArgs a) {
             d4[g] = *reinterpret_cast<const float4*>(&row_d[slot][8 * g + 4 * half]);
         }
     };
-    auto step = [&](int qt, auto slot_c, float4 (&l4)[4], float4 (&d4)[4]) {
+    // One tile; loads(t) issues load t of the next tile into the other slot
+    auto step = [&](int qt, auto slot_c, float4 (&l4)[4], float4 (&d4)[4], auto&& loads) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int QO = slot * C::Q_ELEMS * 2, OO = slot * C::O_ELEMS * 2;  // slot byte offsets
         constexpr int NBV = DV / 32, NBK = DQK / 32;
@@ -639,7 +667,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
                          "v"(d4[g].z), "v"(d4[g].w));
         f32x16 sa[1], dpa[1];
         for (int j = 0; j < 16; ++j) sa[0][j] = dpa[0][j] = 0.f;
-        gemm_rows<E, DQK, 1, QO, 3>(qr, sa, kf, NoSide{});  // S = Q K^T (this lane: one key, 16 rows)
+        gemm_rows<E, DQK, 1, QO, 3>(qr, sa, kf, loads);  // S = Q K^T (this lane: one key, 16 rows)
         f32x16& s = sa[0];
         if (!(qt >= full_lo && qt + kQT - 1 <= full_hi)) {
             const uint32_t base = (uint32_t)(qt + half * 4) - q_first;
@@ -689,24 +717,32 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     // branch around the accumulators).
     const int ntiles = q_hi > q_lo ? (q_hi - q_lo + kQT - 1) / kQT : 0;
     if (ntiles > 0) {
-        issue(q_lo, 0);
+        {
+            const TileRsrc r = rsrc(q_lo);
+            static_for<C::Q_LOADS + C::O_LOADS>([&](auto i_c) { load_one(r, 0, i_c); });
+            issue_rows(q_lo);
+        }
         sync_tiles(0);
         int i = 0;
         float4 l4[4], d4[4];
         for (; i + 2 <= ntiles; i += 2) {
             const int qt = q_lo + i * kQT;
             row_values(0, l4, d4);
-            issue(qt + kQT, 1);
-            step(qt, std::integral_constant<int, 0>{}, l4, d4);
+            issue_rows(qt + kQT);
+            const TileRsrc r1 = rsrc(qt + kQT);
+            step(qt, std::integral_constant<int, 0>{}, l4, d4, [&](auto t_c) { load_one(r1, 1, t_c); });
             sync_tiles(1);
             row_values(1, l4, d4);
-            if (i + 2 < ntiles) issue(qt + 2 * kQT, 0);
-            step(qt + kQT, std::integral_constant<int, 1>{}, l4, d4);
+            // past the last tile the ranges are empty (into a slot no step
+            // reads) and the row values are not used
+            issue_rows(qt + 2 * kQT);
+            const TileRsrc r0 = rsrc(qt + 2 * kQT);
+            step(qt + kQT, std::integral_constant<int, 1>{}, l4, d4, [&](auto t_c) { load_one(r0, 0, t_c); });
             sync_tiles(0);
         }
         if (i < ntiles) {
             row_values(0, l4, d4);
-            step(q_lo + i * kQT, std::integral_constant<int, 0>{}, l4, d4);
+            step(q_lo + i * kQT, std::integral_constant<int, 0>{}, l4, d4, NoSide{});
         }
     }
 
