@@ -9,7 +9,9 @@ forward steps, the backward (sk_attn_backward: dQ, dK, dV of the same
 problem for a seeded dO) is timed on its own and reported under "backward".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--backward-steps N]
+                    [--backward-steps N] [--copy-check]
+    python bench.py --write-traffic FETCH_DIR WRITE_DIR   (traffic file from
+                    two rocprofv3 counter runs; see write_traffic)
 """
 from __future__ import annotations
 
@@ -54,6 +56,78 @@ def measured_traffic():
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def write_traffic(fetch_dir: str, write_dir: str) -> None:
+    """Write TRAFFIC_FILE from two rocprofv3 counter runs of this script
+    with --copy-check: `--pmc FETCH_SIZE` into fetch_dir and `--pmc
+    WRITE_SIZE` into write_dir (csv output, file prefix "run").  Each
+    counter is averaged over the partial kernel's and the piece merge's
+    dispatches and scaled by what it reads for the plain 1 GiB device copy
+    (the largest dispatch that is not one of this library's kernels)."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(d: str, counter: str):
+        vals = defaultdict(float)
+        names = {}
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        return vals, names
+
+    def summarize(d: str, counter: str):
+        vals, names = per_dispatch(d, counter)
+        mine = {"partial_bf16_kernel": [], "merge_pieces_kernel": []}
+        other = []
+        for i, v in vals.items():
+            key = next((k for k in mine if k in names[i]), None)
+            if key:
+                mine[key].append(v)
+            elif "sk::" not in names[i] and "_ZN2sk" not in names[i]:
+                other.append(v)
+        if not all(mine.values()) or not other:
+            raise SystemExit(f"{d}: partial kernel, piece merge or copy dispatch missing")
+        return {k: sum(v) / len(v) for k, v in mine.items()}, max(other)
+
+    fetch, copy_fetch = summarize(fetch_dir, "FETCH_SIZE")
+    write, copy_write = summarize(write_dir, "WRITE_SIZE")
+    gib = 1 << 30
+    fetch_scale = gib / (copy_fetch * 1024.0)
+    write_scale = gib / (copy_write * 1024.0)
+    total = sum(fetch.values()) * 1024.0 * fetch_scale + sum(write.values()) * 1024.0 * write_scale
+    from split_kv_attention_amd import workloads
+
+    w = workloads.LONG_PREFILL
+    H, Sq, Sk, S = w.heads, w.sq[0], w.sk[0], w.split_kv
+    algorithmic = Sq * H * w.d_qk * 2 + Sk * H * (w.d_qk + w.d_v) * 2 + S * H * Sq * (w.d_v + 1) * 4
+    out = {
+        "kernel": "sk_attn_partial: partial_bf16_kernel<192,128> + merge_pieces_kernel<128>",
+        "workload": w.name,
+        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_sources": PARTIAL_SOURCES,
+        "fetch_size_kib_per_dispatch": fetch,
+        "write_size_kib_per_dispatch": write,
+        "copy_reference": {"bytes_read": gib, "bytes_written": gib, "fetch_size_kib": copy_fetch,
+                           "write_size_kib": copy_write},
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "hbm_bytes_per_launch": round(total),
+        "algorithmic_bytes_per_launch": algorithmic,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py "
+            "--no-cpu-baseline --steps 3 --warmup 1 --cold-iters 1 --backward-steps 1 --copy-check",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py "
+            "--no-cpu-baseline --steps 3 --warmup 1 --cold-iters 1 --backward-steps 1 --copy-check",
+            f"python3 bench.py --write-traffic {fetch_dir} {write_dir}",
+        ],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 12.0):
@@ -159,7 +233,12 @@ def main() -> int:
     ap.add_argument("--backward-steps", type=int, default=10, help="timed backward calls (0: skip)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the partial kernel's HBM traffic file from two rocprofv3 counter runs, then exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)
@@ -284,6 +363,7 @@ def main() -> int:
             "gbps_in_pipeline": combine_bytes / (t_combine * 1e-3) / 1e9,
             "gbps_cold_cache": combine_bytes / (t_combine_cold * 1e-3) / 1e9,
             "frac_cold_cache": combine_bytes / (t_combine_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "frac_in_pipeline": combine_bytes / (t_combine * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "peak": PEAK_HBM_GBPS,
         },
         "counts_ms": t_counts,
