@@ -58,13 +58,14 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def write_traffic(fetch_dir: str, write_dir: str) -> None:
-    """Write TRAFFIC_FILE from two rocprofv3 counter runs of this script
-    with --copy-check: `--pmc FETCH_SIZE` into fetch_dir and `--pmc
-    WRITE_SIZE` into write_dir (csv output, file prefix "run").  Each
-    counter is averaged over the partial kernel's and the piece merge's
-    dispatches and scaled by what it reads for the plain 1 GiB device copy
-    (the largest dispatch that is not one of this library's kernels)."""
+def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> dict:
+    """Write the traffic file (TRAFFIC_FILE unless `path` is given) from two
+    rocprofv3 counter runs of this script with --copy-check: `--pmc
+    FETCH_SIZE` into fetch_dir and `--pmc WRITE_SIZE` into write_dir (csv
+    output, file prefix "run").  Each counter is averaged over the partial
+    kernel's and the piece merge's dispatches and scaled by what it reads
+    for the plain 1 GiB device copy (the largest dispatch that is not one of
+    this library's kernels)."""
     import csv
     from collections import defaultdict
 
@@ -125,9 +126,9 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
             f"python3 bench.py --write-traffic {fetch_dir} {write_dir}",
         ],
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    return out
 
 
 def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 12.0):
@@ -237,7 +238,7 @@ def main() -> int:
                     help="write the partial kernel's HBM traffic file from two rocprofv3 counter runs, then exit")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        print(json.dumps(write_traffic(*args.write_traffic), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",

@@ -1,0 +1,61 @@
+"""bench.py's traffic file from rocprofv3 counter CSVs (host logic, no GPU)."""
+import csv
+import importlib.util
+import json
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(d, counter, rows):
+    os.makedirs(d)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, vals) in enumerate(rows):
+            for v in vals:  # one line per XCD-level instance: summed per dispatch
+                w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_write_traffic_scales_by_the_copy(tmp_path):
+    bench = _bench()
+    part = "_ZN2sk12_GLOBAL__N_119partial_bf16_kernelIDF16bLi192ELi128EEEvNS_11PartialArgsE"
+    merge = "void sk::(anonymous namespace)::merge_pieces_kernel<128>(sk::PartialArgs)"
+    comb = "_ZN2sk14combine_kernelIDF16bLi4ELb1EEEvNS_11CombineArgsE"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    # two dispatches of the partial kernel (mean 300 KiB), one merge, a
+    # larger combine that must not count, and the copy read as half its size
+    _write(fetch, "FETCH_SIZE", [(part, [100.0, 150.0]), (part, [200.0, 150.0]), (merge, [10.0]),
+                                 (comb, [5e5]), (copy, [262144.0, 262144.0])])
+    _write(write, "WRITE_SIZE", [(part, [40.0]), (part, [60.0]), (merge, [4.0]), (comb, [7e5]),
+                                 (copy, [1048576.0]), ("zero_fill", [1048576.0])])
+    out = bench.write_traffic(fetch, write, path=str(tmp_path / "t.json"))
+    assert out["fetch_size_kib_per_dispatch"] == {"partial_bf16_kernel": 300.0, "merge_pieces_kernel": 10.0}
+    assert out["write_size_kib_per_dispatch"] == {"partial_bf16_kernel": 50.0, "merge_pieces_kernel": 4.0}
+    assert out["fetch_scale"] == 2.0 and out["write_scale"] == 1.0
+    assert out["hbm_bytes_per_launch"] == (310 * 2 + 54) * 1024
+    assert out["kernel_source_sha256"] == bench.kernel_source_hash()
+    with open(tmp_path / "t.json") as f:
+        assert json.load(f) == out
+
+
+def test_write_traffic_needs_every_kernel(tmp_path):
+    import pytest
+
+    bench = _bench()
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    _write(fetch, "FETCH_SIZE", [("partial_bf16_kernel", [1.0]), ("copy", [2.0])])
+    _write(write, "WRITE_SIZE", [("partial_bf16_kernel", [1.0]), ("copy", [2.0])])
+    with pytest.raises(SystemExit):
+        bench.write_traffic(fetch, write, path=str(tmp_path / "t.json"))
