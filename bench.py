@@ -12,6 +12,7 @@ problem for a seeded dO) is timed on its own and reported under "backward".
                     [--backward-steps N] [--copy-check]
     python bench.py --write-traffic FETCH_DIR WRITE_DIR   (traffic file from
                     two rocprofv3 counter runs; see write_traffic)
+    python bench.py --sweep    (every parity workload, one JSON line each)
 """
 from __future__ import annotations
 
@@ -131,6 +132,98 @@ def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> d
     return out
 
 
+def visible_pairs(w) -> int:
+    """(query, key) pairs the mask leaves visible, per head: row q of
+    sequence b sees keys 0 .. min(q + offset_b, lastValid_b) (no mask: 0 ..
+    lastValid_b), lastValid_b = Sk_b - 1 unless given."""
+    import numpy as np
+
+    total = 0
+    for b, (sq, sk) in enumerate(zip(w.sq, w.sk)):
+        lv = w.last_valid_per_seq[b] if w.last_valid_per_seq else w.last_valid_kv_index
+        lv = sk - 1 if lv < 0 else min(lv, sk - 1)
+        q = np.arange(sq, dtype=np.int64)
+        if w.mask == "none":
+            last = np.full(sq, lv, dtype=np.int64)
+        else:
+            off = 0 if w.mask == "causal" else (w.prefix_offset_per_seq[b] if w.prefix_offset_per_seq
+                                                  else w.prefix_offset)
+            last = np.minimum(q + off, lv)
+        total += int(np.clip(last + 1, 0, sk).sum())
+    return total
+
+
+def sweep() -> None:
+    """Every workload of the parity suite through counts -> partial ->
+    combine, medians of HIP-event timings on one stream; one JSON line per
+    workload with the partial's rate against its roofline (bf16 MFMA or
+    HBM, whichever bounds it; the f32 kernel against the fp32 vector peak)
+    and the combine's against HBM."""
+    import numpy as np
+    import torch
+
+    from split_kv_attention_amd import _lib, attention, workloads
+
+    torch.cuda.set_device(0)
+    for w in workloads.CONFIGS:
+        inputs = workloads.make_inputs(w, "cuda:0", seed=3)
+        prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+        counts, o_part, lse_part, out, lse_out = attention.alloc_outputs(prob, inputs["q"], inputs["v"])
+        stream = torch.cuda.current_stream()
+        sh = stream.cuda_stream
+        q, k, v = inputs["q"], inputs["k"], inputs["v"]
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            _lib.sk_valid_split_counts(prob.c, counts, sh)
+            if ev:
+                ev[1].record(stream)
+            _lib.sk_attn_partial(prob.c, q, k, v, o_part, lse_part, sh)
+            if ev:
+                ev[2].record(stream)
+            _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
+            if ev:
+                ev[3].record(stream)
+
+        n = 20 if sum(w.sk) * w.heads * w.batch > 1e8 else 50
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for i in range(n):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t_part = sorted(e[1].elapsed_time(e[2]) for e in evs)[n // 2]
+        t_comb = sorted(e[2].elapsed_time(e[3]) for e in evs)[n // 2]
+
+        H, es = w.heads, q.element_size()
+        rows = sum(w.sq)
+        keys = sum(w.sk) if w.packed else w.batch * w.sk[0]
+        splits = w.split_kv_per_seq or (w.split_kv,) * w.batch
+        flop = 2.0 * (w.d_qk + w.d_v) * H * visible_pairs(w)
+        part_bytes = (rows * w.d_qk + keys * (w.d_qk + w.d_v)) * H * es + \
+            sum(s * r for s, r in zip(splits, w.sq)) * H * (w.d_v + 1) * 4
+        c = counts.cpu().numpy().astype(np.int64)
+        comb_bytes = int(c.sum()) * H * (w.d_v * 4 + 4) + rows * 4 + rows * H * (w.d_v * out.element_size() + 4)
+        if w.dtype == "f32":
+            bound, peak, unit, achieved = "alu", 157.3, "TFLOP/s", flop / (t_part * 1e-3) / 1e12
+        elif flop / part_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+            bound, peak, unit, achieved = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s", flop / (t_part * 1e-3) / 1e12
+        else:
+            bound, peak, unit, achieved = "hbm", PEAK_HBM_GBPS, "GB/s", part_bytes / (t_part * 1e-3) / 1e9
+        comb_gbps = comb_bytes / (t_comb * 1e-3) / 1e9
+        print(json.dumps({
+            "workload": w.name, "calls": n,
+            "partial": {"ms": t_part, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                        "frac": achieved / peak, "flop": flop, "algorithmic_bytes": part_bytes},
+            "combine": {"ms": t_comb, "gbps": comb_gbps, "frac": comb_gbps / PEAK_HBM_GBPS,
+                        "algorithmic_bytes": comb_bytes},
+        }), flush=True)
+        del inputs, prob, counts, o_part, lse_part, out, lse_out, q, k, v
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 12.0):
     """The oracle (as it stands) on a bounded sample of the same workload:
     the full split method (counts, partials at the kernel's query block,
@@ -234,6 +327,8 @@ def main() -> int:
     ap.add_argument("--backward-steps", type=int, default=10, help="timed backward calls (0: skip)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload of the parity suite (one JSON line each), then exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the partial kernel's HBM traffic file from two rocprofv3 counter runs, then exit")
     args = ap.parse_args()
@@ -244,6 +339,9 @@ def main() -> int:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)
         return 2
+    if args.sweep:
+        sweep()
+        return 0
 
     import torch
 
