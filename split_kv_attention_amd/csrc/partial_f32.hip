@@ -6,18 +6,41 @@
 // partials on the host" (Summary; the block partition in "Per-row valid-split
 // counts").  gfx950 has no reduced-precision f32 matrix path that would keep
 // an f32 problem at f32 accuracy, so this variant uses FMA on the vector ALUs:
-// one lane per query row, key/value tiles staged through LDS and read as
-// wave-wide broadcasts.  It serves small f32 problems; bf16 goes to MFMA.
+// SUB lanes per query row (four, at least four values each), each holding
+// a slice of the row's Q and of its output, with key/value tiles staged
+// through LDS.  A score is SUB partial dot products summed across the row's
+// lanes.  It serves small f32 problems; bf16 goes to MFMA.
 #include "sk_common.hpp"
 
 namespace sk {
 
 namespace {
 
-constexpr int kF32Rows = 64;  // query rows per workgroup (one wave)
+constexpr int kF32Rows = 64;  // query rows per workgroup
+
+// Lanes per query row for head dims DQK, DV: four, or fewer where a lane
+// would not get a whole float4 slice.  (On the tiny 64-dim workload four
+// lanes per row took the kernel from 43 to 23 us, sixteen to 27 us.)
+template <int DQK, int DV>
+constexpr int f32_sub() {
+    constexpr int d = DQK < DV ? DQK : DV;
+    return d / 4 < 4 ? d / 4 : 4;
+}
+
+// Sum over the SUB consecutive lanes of a row (xor butterfly within each
+// group of SUB lanes).
+template <int SUB>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < SUB; m <<= 1) x += __shfl_xor(x, m, SUB);
+    return x;
+}
 
 template <int DQK, int DV, int BN>
-__global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
+__global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_kernel(PartialArgs a) {
+    constexpr int SUB = f32_sub<DQK, DV>(), NT = kF32Rows * SUB;
+    constexpr int QS = DQK / SUB, VS = DV / SUB;  // this lane's slice of a Q / output row
+    static_assert(QS % 4 == 0 && VS % 4 == 0, "whole float4 slices");
     __shared__ float4 Ks[BN * DQK / 4];
     __shared__ float4 Vs[BN * DV / 4];
 
@@ -42,44 +65,45 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
         if (lo_first > ks) ks = (int)min((int64_t)ke, ks + (lo_first - ks) / BN * BN);
     }
 
-    const int lane = threadIdx.x;
-    const int qrow = r0 + lane;
+    const int tid = threadIdx.x;
+    const int sub = tid % SUB;
+    const int qrow = r0 + tid / SUB;
     const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
     const int64_t vis = vis_last(sq, mask, qrow);
     const int64_t lo = vis_first(sq, win, qrow);
 
     const float* qp = reinterpret_cast<const float*>(a.q) +
                       (a.seqs.cu_q ? (sq.row0 + qrow) * a.q_row : (int64_t)it.batch * a.q_batch + (int64_t)qrow * a.q_row) +
-                      (int64_t)it.head * a.q_head;
+                      (int64_t)it.head * a.q_head + sub * QS;
     const float* kp = reinterpret_cast<const float*>(a.k) +
                       (sq.krow0 >= 0 ? sq.krow0 * a.k_row : (int64_t)it.batch * a.k_batch) + (int64_t)it.head * a.k_head;
     const float* vp = reinterpret_cast<const float*>(a.v) +
                       (sq.krow0 >= 0 ? sq.krow0 * a.v_row : (int64_t)it.batch * a.v_batch) + (int64_t)it.head * a.v_head;
 
-    float qv[DQK];
+    float qv[QS];
 #pragma unroll
-    for (int d = 0; d < DQK; d += 4) {
+    for (int d = 0; d < QS; d += 4) {
         float4 x = row_ok ? *reinterpret_cast<const float4*>(qp + d) : make_float4(0.f, 0.f, 0.f, 0.f);
         qv[d] = x.x;
         qv[d + 1] = x.y;
         qv[d + 2] = x.z;
         qv[d + 3] = x.w;
     }
-    float o[DV];
+    float o[VS];
 #pragma unroll
-    for (int d = 0; d < DV; ++d) o[d] = 0.f;
+    for (int d = 0; d < VS; ++d) o[d] = 0.f;
     float m = -INFINITY, l = 0.f;
     const float c = a.scale_log2;
 
     for (int kt = ks; kt < ke; kt += BN) {
         __syncthreads();
-        for (int i = lane; i < BN * DQK / 4; i += kF32Rows) {
+        for (int i = tid; i < BN * DQK / 4; i += NT) {
             const int kr = i / (DQK / 4), col = i % (DQK / 4);
             const int key = kt + kr;
             Ks[i] = key < ke ? *reinterpret_cast<const float4*>(kp + (int64_t)key * a.k_row + col * 4)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        for (int i = lane; i < BN * DV / 4; i += kF32Rows) {
+        for (int i = tid; i < BN * DV / 4; i += NT) {
             const int kr = i / (DV / 4), col = i % (DV / 4);
             const int key = kt + kr;
             Vs[i] = key < ke ? *reinterpret_cast<const float4*>(vp + (int64_t)key * a.v_row + col * 4)
@@ -93,19 +117,21 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
         for (int j = 0; j < BN; ++j) {
             float dot = 0.f;
 #pragma unroll
-            for (int d = 0; d < DQK / 4; ++d) {
-                const float4 kk = Ks[j * (DQK / 4) + d];
+            for (int d = 0; d < QS / 4; ++d) {
+                const float4 kk = Ks[j * (DQK / 4) + sub * (QS / 4) + d];
                 dot = fmaf(qv[4 * d], kk.x, dot);
                 dot = fmaf(qv[4 * d + 1], kk.y, dot);
                 dot = fmaf(qv[4 * d + 2], kk.z, dot);
                 dot = fmaf(qv[4 * d + 3], kk.w, dot);
             }
+            dot = row_sum<SUB>(dot);
             const int key = kt + j;
             sc[j] = (key < ke && key <= vis && key >= lo) ? dot : -INFINITY;
             mx = fmaxf(mx, sc[j]);
         }
         // Online softmax in base 2; a row with nothing visible yet keeps
-        // m = -inf and zero weights (no -inf - -inf).
+        // m = -inf and zero weights (no -inf - -inf).  The row's lanes hold
+        // the same scores and take the same steps.
         const float m_new = fmaxf(m, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = exp2f((m - m_use) * c);
@@ -119,11 +145,11 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
         l = fmaf(l, alpha, rs);
         m = m_new;
 #pragma unroll
-        for (int d = 0; d < DV / 4; ++d) {
+        for (int d = 0; d < VS / 4; ++d) {
             float4 acc = make_float4(o[4 * d] * alpha, o[4 * d + 1] * alpha, o[4 * d + 2] * alpha, o[4 * d + 3] * alpha);
 #pragma unroll
             for (int j = 0; j < BN; ++j) {
-                const float4 vv = Vs[j * (DV / 4) + d];
+                const float4 vv = Vs[j * (DV / 4) + sub * (VS / 4) + d];
                 acc.x = fmaf(sc[j], vv.x, acc.x);
                 acc.y = fmaf(sc[j], vv.y, acc.y);
                 acc.z = fmaf(sc[j], vv.z, acc.z);
@@ -143,16 +169,16 @@ __global__ __launch_bounds__(kF32Rows) void partial_f32_kernel(PartialArgs a) {
     const bool empty = (m == -INFINITY);
     const float inv = empty ? 0.f : 1.0f / l;
     const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
-    float* op = a.o_part + slot * DV;
+    float* op = a.o_part + slot * DV + sub * VS;
 #pragma unroll
-    for (int d = 0; d < DV; d += 4)
+    for (int d = 0; d < VS; d += 4)
         *reinterpret_cast<float4*>(op + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-    a.lse_part[slot] = empty ? -INFINITY : m * a.scale + logf(l);
+    if (sub == 0) a.lse_part[slot] = empty ? -INFINITY : m * a.scale + logf(l);
 }
 
 template <int DQK, int DV, int BN>
 hipError_t launch(const PartialArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((partial_f32_kernel<DQK, DV, BN>), dim3(a.n_work), dim3(kF32Rows), 0, stream, a);
+    hipLaunchKernelGGL((partial_f32_kernel<DQK, DV, BN>), dim3(a.n_work), dim3(kF32Rows * f32_sub<DQK, DV>()), 0, stream, a);
     return hipGetLastError();
 }
 
