@@ -1,4 +1,5 @@
-"""bench.py's traffic file from rocprofv3 counter CSVs (host logic, no GPU)."""
+"""bench.py host logic (no GPU): the traffic file from rocprofv3 counter CSVs
+and the FLOP accounting."""
 import csv
 import importlib.util
 import json
@@ -59,3 +60,19 @@ def test_write_traffic_needs_every_kernel(tmp_path):
     _write(write, "WRITE_SIZE", [("partial_bf16_kernel", [1.0]), ("copy", [2.0])])
     with pytest.raises(SystemExit):
         bench.write_traffic(fetch, write, path=str(tmp_path / "t.json"))
+
+
+def test_visible_pairs_match_the_oracle():
+    """bench.py's FLOP accounting counts the pairs the oracle's visibility
+    rule leaves visible, on every workload of the parity suite."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    from oracle import adapter
+    from oracle import splitkv as oracle
+    from split_kv_attention_amd import workloads
+
+    bench = _bench()
+    for w in workloads.CONFIGS:
+        expect = sum(oracle.visible_pairs(s) for s in adapter.seq_specs(w))
+        assert bench.visible_pairs(w) == expect, w.name
