@@ -76,3 +76,15 @@ def test_visible_pairs_match_the_oracle():
     for w in workloads.CONFIGS:
         expect = sum(oracle.visible_pairs(s) for s in adapter.seq_specs(w))
         assert bench.visible_pairs(w) == expect, w.name
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py runs on one GPU; --gpus N > 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
