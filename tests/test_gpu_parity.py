@@ -440,6 +440,22 @@ def test_full_prefill_sampled_rows(w):
     torch.cuda.empty_cache()
 
 
+def test_full_prefill_f16_sampled_rows():
+    """f16 storage at the long-context prefill's full size (H = 12, Sq = 4096,
+    Sk = 42700, split 3) in the benchmark's launch configuration: sampled
+    rows (tile edges and random) of three heads against the oracle."""
+    w = _shrink(workloads.LONG_PREFILL, name="varlen_prefill_f16_H12_Sq4096_Sk42700_D192x128_S3", dtype="f16")
+    log(f"full {w.name}")
+    inputs, prob, res = run_gpu(w)
+    assert res["out"].dtype == torch.float16
+    rows_per_seq = {0: sample_rows(w.sq[0], 12, seed=5, tile=prob.m_per_block)}
+    st = compare(w, inputs, prob, res, rows_per_seq=rows_per_seq, heads=[0, 6, 11], label=w.name)
+    log(f"  {st}")
+    assert torch.isfinite(res["out"]).all()
+    del inputs, res
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("w", [workloads.LONG_PREFILL, workloads.VARLEN_BATCH_PREFIX], ids=lambda w: w.name)
 def test_full_prefill_every_row_and_head(w):
     """The long-context prefill (H = 12, Sq = 4096, Sk = 42700, split 3) and
