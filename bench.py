@@ -224,40 +224,148 @@ def sweep() -> None:
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 12.0):
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    the full split method (counts, partials at the kernel's query block,
-    merge) for chunks of query rows over all heads and all 42700 keys, until
-    `budget_s` of wall time."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
-    from oracle import adapter
 
+def _blas_info() -> str:
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs) or "unknown"
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    host = {k: v.cpu() for k, v in inputs.items()}
-    rng = np.random.default_rng(0)
-    order = rng.permutation(w.sq[0])
-    done = 0
+        return "unknown"
+
+
+def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_workers: int = 16):
+    """The oracle (as it stands) timed on the host's cores over the whole
+    workload: units of (sequence, head, 32 query rows), each the full split
+    method (counts, partials at the kernel's query block, merge) against all
+    of the sequence's keys, run on a thread pool with one BLAS thread per
+    worker and as many workers as the process may use (its CPU affinity,
+    capped at the GPU's 16-core share).  Units run in a seeded random order;
+    if the wall-clock budget runs out first, the finished units are the
+    sample and the rate is scaled from them."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor, wait, FIRST_COMPLETED
+    from threadpoolctl import threadpool_limits
+
+    from oracle import adapter
+
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, max_workers))
+    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in inputs.items()}
     chunk = 32
+    units = [(b, h, r0) for b in range(len(w.sq)) for h in range(w.heads) for r0 in range(0, w.sq[b], chunk)]
+    order = np.random.default_rng(0).permutation(len(units))
+
+    def run_unit(i):
+        b, h, r0 = units[i]
+        rows = np.arange(r0, min(r0 + chunk, w.sq[b]))
+        adapter.expected(w, host, m_per_block, rows_per_seq={bb: (rows if bb == b else rows[:0])
+                                                              for bb in range(len(w.sq))}, heads=[h])
+        return float(len(rows)) * w.sk[b]  # (query, key) pairs, every key visible (no mask)
+
+    pairs = 0.0
+    done = 0
     t0 = time.perf_counter()
-    while done < len(order) and time.perf_counter() - t0 < budget_s:
-        rows = np.sort(order[done : done + chunk])
-        adapter.expected(w, host, m_per_block, rows_per_seq={0: rows})
-        done += len(rows)
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        it = iter(order)
+        pending = set()
+        for _ in range(2 * workers):
+            i = next(it, None)
+            if i is not None:
+                pending.add(ex.submit(run_unit, int(i)))
+        while pending:
+            fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in fin:
+                pairs += f.result()
+                done += 1
+            if time.perf_counter() - t0 < budget_s:
+                for _ in fin:
+                    i = next(it, None)
+                    if i is not None:
+                        pending.add(ex.submit(run_unit, int(i)))
     dt = time.perf_counter() - t0
-    flops = 2.0 * (w.d_qk + w.d_v) * w.heads * done * w.sk[0]
+    flops = 2.0 * (w.d_qk + w.d_v) * pairs
+    full = done == len(units)
+    what = "the whole workload" if full else f"{done} of {len(units)} units (seeded random order; budget {budget_s:.0f} s)"
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{done} of {w.sq[0]} query rows x {w.heads} heads x {w.sk[0]} keys (full method, f64, "
-                  f"{dt:.1f} s on {platform.processor() or platform.machine()})",
+        "sample": f"{what}: units of (sequence, head, {chunk} query rows) x all {w.sk[0]} keys, full split method "
+                  f"in f64, {dt:.1f} s wall on a {workers}-thread pool, one BLAS thread each",
+        "seconds": dt,
+        "units_done": done,
+        "units_total": len(units),
+        "cpu_model": _cpu_model(),
+        "affinity_cpus": affinity,
+        "numpy": np.__version__,
+        "blas": _blas_info(),
+    }
+
+
+def time_unsplit(w, inputs, stream, steps: int, t_partial_split: float, t_combine_split: float, warmup: int):
+    """The same inputs through the same kernels with split_kv = 1 (one
+    partial per row, the combine a plain cast), timed with HIP events like
+    the split path: the comparison the aiter page's "Test Result" makes
+    between its unsplit and split-3 kernels (MI325X: 3.065 ms and 2.269 ms,
+    26% faster; another machine, quoted as context only)."""
+    import dataclasses
+
+    import torch
+
+    from split_kv_attention_amd import _lib, attention, workloads
+
+    w1 = dataclasses.replace(w, split_kv=1)
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w1, inputs))
+    counts, o_part, lse_part, out, lse_out = attention.alloc_outputs(prob, inputs["q"], inputs["v"])
+    q, k, v = inputs["q"], inputs["k"], inputs["v"]
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        _lib.sk_valid_split_counts(prob.c, counts, sh)
+        if ev:
+            ev[0].record(stream)
+        _lib.sk_attn_partial(prob.c, q, k, v, o_part, lse_part, sh)
+        if ev:
+            ev[1].record(stream)
+        _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(max(3, min(warmup, 10))):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_part = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    t_comb = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    H, Sq, Sk = w.heads, w.sq[0], w.sk[0]
+    flops = 2.0 * (w.d_qk + w.d_v) * H * Sq * Sk
+    split_total = t_partial_split + t_combine_split
+    return {
+        "split_kv": 1,
+        "ms_partial": t_part,
+        "ms_combine": t_comb,
+        "ms_partial_plus_combine": t_part + t_comb,
+        "tflops_partial_plus_combine": flops / ((t_part + t_comb) * 1e-3) / 1e12,
+        "split_ms_partial_plus_combine": split_total,
+        "split_speedup": (t_part + t_comb) / split_total,
+        "split_time_saved_frac": 1.0 - split_total / (t_part + t_comb),
+        "pages_context_mi325x": {"unsplit_ms": 3.065, "split3_ms": 2.269, "split_time_saved_frac": 0.26},
     }
 
 
@@ -402,6 +510,8 @@ def main() -> int:
     t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
     del flush
 
+    unsplit = time_unsplit(w, inputs, stream, args.steps, t_partial, t_combine, args.warmup)
+
     backward = None
     if args.backward_steps > 0:
         backward = time_backward(w, prob, inputs, out, lse_out, stream, args.backward_steps)
@@ -466,6 +576,7 @@ def main() -> int:
             "peak": PEAK_HBM_GBPS,
         },
         "counts_ms": t_counts,
+        "unsplit": unsplit,
         "attention_tflops_partial_plus_combine": flops / ((t_partial + t_combine) * 1e-3) / 1e12,
         "backward": backward,
         "cpu_baseline": None,

@@ -190,8 +190,9 @@ sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stre
  * block's last row.  A split that holds keys for the block but none the row
  * may see writes O_s = 0, L_s = -inf.  A split with no key for the whole
  * block is skipped without writing anything (real early exit, rocmlirTriton
- * page, review note on early exit): its slots keep their old contents and
- * sk_attn_combine never reads them.  So the buffers need no clearing.
+ * page, review note on early exit): its slots keep their old contents, and
+ * sk_attn_combine leaves them out of the merge.  So the buffers need no
+ * clearing.
  * q, k, v: device, dtype; o_part, lse_part: device f32, layout in the header,
  * at least sk_workspace_bytes() bytes. */
 sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v,
@@ -203,10 +204,13 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
  *   w_s = exp(L_s - m)
  *   O   = sum_{s<c} w_s O_s / max(sum_{s<c} w_s, 1)      (cast to out_dtype last)
  *   LSE = m + ln(sum_{s<c} w_s), or -inf when the sum is 0
- * Splits s >= c are never read, and neither are the splits sk_attn_partial
- * skipped: c is first capped at the number of splits that hold a key for the
- * row's M block (the block partition of sk_partial_m_per_block; the skipped
- * ones would have weight 0).  counts: device int32 [rows] from
+ * Splits s >= c take no part in the merge, and neither do the splits
+ * sk_attn_partial skipped: c is first capped at the number of splits that
+ * hold a key for the row's M block (the block partition of
+ * sk_partial_m_per_block; the skipped ones would have weight 0).  To keep
+ * its loads in flight together, the kernel loads the slots of a row's first
+ * splits (up to 4, 8, 16 or 32 by S_max) before it knows c, so slots past c
+ * may be read; whatever they hold never reaches the result.  counts: device int32 [rows] from
  * sk_valid_split_counts, or NULL to evaluate the same formula inline.
  * out: device out_dtype with the o_stride_* layout, fully overwritten (a fully
  * masked row becomes 0).  lse_out: device f32 [num_heads][rows], or NULL to

@@ -173,11 +173,12 @@ def valid_split_counts(spec: SeqSpec, rows=None) -> np.ndarray:
 def block_split_ranges(spec: SeqSpec, m_per_block: int, block: int):
     """Key range [start, end) of every split for query block `block`.
 
-    The kernel partitions each M block's keys using the block's last row
-    [R, Per-row valid-split counts, the paragraph on conservative counts]:
-    the same keysPerSplit formula evaluated at that row, split s covering
-    keys [s * kps, min((s + 1) * kps, rowLast + 1)).  Reading: "the block's
-    last row" is the last row that exists, min(start + mPB, sq) - 1.
+    One partition serves every row of an M block: keysPerSplit is taken
+    from the count formula at the block's final row, and split s then holds
+    keys [s * kps, min((s + 1) * kps, rowLast + 1)) of that row's visible
+    range [R, Per-row valid-split counts, the paragraph on conservative
+    counts].  Reading: the final row is the last one that exists,
+    min(start + mPB, sq) - 1.
     """
     last = min((block + 1) * m_per_block, spec.sq) - 1
     rl = int(row_last([last], spec)[0])

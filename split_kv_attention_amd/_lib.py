@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsplitkv.so")
+# SPLITKV_LIBRARY names another build of the same library (the host-side
+# AddressSanitizer build of split_kv_attention_amd.build.build_asan).
+LIB_PATH = os.environ.get("SPLITKV_LIBRARY") or os.path.join(_PKG, "libsplitkv.so")
 
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_HIP = 0, 1, 2, 3
 SK_MASK_NONE, SK_MASK_CAUSAL, SK_MASK_PREFIX_CAUSAL = 0, 1, 2

@@ -3,6 +3,11 @@
 Every call recompiles: each translation unit under csrc/ goes to an object
 file in _build/, then they are linked into split_kv_attention_amd/libsplitkv.so.
 Usage:  python -m split_kv_attention_amd.build   (or __graft_entry__.build()).
+
+build_asan() makes a second copy of the library whose HOST code is built with
+AddressSanitizer (device code unchanged) in _build/asan/; a process that loads
+it must preload the sanitizer runtime (asan_runtime()).  It exists for the
+host-side tests of argument checking and dispatch.
 """
 from __future__ import annotations
 
@@ -48,8 +53,8 @@ def sources():
     )
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = BUILD) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [hipcc(), *HIP_FLAGS, *extra, *lang, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -74,6 +79,41 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH
+
+
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libsplitkv_asan.so")
+# Host-only instrumentation: each sanitizer flag applies to the host pass only.
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the AddressSanitizer runtime of the compiler hipcc drives."""
+    llvm = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "lib", "clang")
+    if not os.path.isdir(llvm):
+        llvm = "/opt/rocm/llvm/lib/clang"
+    for ver in sorted(os.listdir(llvm), reverse=True):
+        p = os.path.join(llvm, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return os.path.realpath(p)
+    raise RuntimeError("AddressSanitizer runtime (libclang_rt.asan-x86_64.so) not found")
+
+
+def build_asan() -> str:
+    """Compile every source with the host pass under AddressSanitizer and link
+    _build/asan/libsplitkv_asan.so; returns its path.  The shared library
+    leaves the sanitizer's symbols to the preloaded runtime."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, ASAN_HOST_FLAGS, ASAN_DIR), srcs))
+    tmp = ASAN_LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
 
 
 if __name__ == "__main__":
