@@ -16,7 +16,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library allocates, frees and synchronises nothing; it only enqueues
  *     kernels on `stream` (a hipStream_t passed as void*, NULL = the null
- *     stream).  Calls are asynchronous and thread-safe.
+ *     stream).  Calls are asynchronous and thread-safe, except
+ *     sk_attn_partial_noalloc, whose calls on one GPU share the library's
+ *     own scratch (see there).
  *   - Arguments are checked on the host before anything is enqueued.  An
  *     invalid argument returns SK_ERR_INVALID_ARG, a valid request this
  *     build does not implement returns SK_ERR_UNSUPPORTED, and a failed
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SK_ABI_VERSION 4
+#define SK_ABI_VERSION 5
 
 typedef enum sk_status {
     SK_OK = 0,
@@ -197,6 +199,22 @@ sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stre
  * at least sk_workspace_bytes() bytes. */
 sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v,
                           float* o_part, float* lse_part, void* stream);
+
+/* sk_attn_partial for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as sk_attn_partial, except that the
+ * load-balance scratch is the library's own instead of
+ * p->partial_scratch (which is ignored): a static device array of 36 MiB
+ * (37748736 bytes) that every GPU the library is loaded on holds until the
+ * process ends.  It calls no allocator.  A problem whose worst-case piece
+ * scratch, sk_partial_scratch_bytes(p), exceeds that size returns
+ * SK_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array and leaves the last call's contents in it (calls
+ * need nothing cleared: each piece is written before it is read), so calls
+ * that can overlap on one GPU (other streams, other threads) race and must
+ * not be made. */
+sk_status sk_attn_partial_noalloc(const sk_problem* p, const void* q, const void* k, const void* v,
+                                  float* o_part, float* lse_part, void* stream);
 
 /* NaN-safe f32 merge of the partials (rocmlirTriton page, "NaN-safe merge" and
  * "f32 merge for f16/bf16"), per (row, head) with c = count of the row:

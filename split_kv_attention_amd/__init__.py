@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     sk_attn_backward,
     sk_attn_combine,
     sk_attn_partial,
+    sk_attn_partial_noalloc,
     sk_backward_workspace_bytes,
     sk_last_error,
     sk_partial_m_per_block,

@@ -31,6 +31,7 @@ EXPORTS = (
     "sk_partial_m_per_block",
     "sk_valid_split_counts",
     "sk_attn_partial",
+    "sk_attn_partial_noalloc",
     "sk_attn_combine",
     "sk_attn_backward",
     "sk_backward_workspace_bytes",
@@ -123,6 +124,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sk_valid_split_counts.argtypes = [P, vp, vp]
     lib.sk_attn_partial.restype = ctypes.c_int
     lib.sk_attn_partial.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.sk_attn_partial_noalloc.restype = ctypes.c_int
+    lib.sk_attn_partial_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sk_attn_combine.restype = ctypes.c_int
     lib.sk_attn_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sk_attn_backward.restype = ctypes.c_int
@@ -216,6 +219,14 @@ def sk_valid_split_counts(problem: SkProblem, counts, stream=None) -> None:
 def sk_attn_partial(problem: SkProblem, q, k, v, o_part, lse_part, stream=None) -> None:
     _check(
         load().sk_attn_partial(
+            ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), _stream(stream)
+        )
+    )
+
+
+def sk_attn_partial_noalloc(problem: SkProblem, q, k, v, o_part, lse_part, stream=None) -> None:
+    _check(
+        load().sk_attn_partial_noalloc(
             ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), _stream(stream)
         )
     )

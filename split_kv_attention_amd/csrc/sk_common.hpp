@@ -99,6 +99,12 @@ __device__ __forceinline__ int32_t valid_split_count(const Seq& s, int mask, int
 // Most key pieces one tail item of the partial kernel is split into.
 constexpr int kMaxPieces = 16;
 
+// The library's own device scratch (static_scratch.hip), which
+// sk_attn_partial_noalloc uses for the last round's key pieces: its size,
+// and its address on the current device (looked up once per device).
+constexpr int64_t kStaticScratchBytes = (int64_t)36 << 20;
+hipError_t static_scratch(void** out);
+
 // Key range [ks, ke) of split `split` for the query block whose last row is
 // last_row: the count formula at that row gives keys per split, split s
 // covers [s*kps, (s+1)*kps) of the keys 0..rowLast, and keys past lastValid

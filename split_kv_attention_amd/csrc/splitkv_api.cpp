@@ -150,18 +150,19 @@ struct TailPlan {
     uint32_t n_main;
     int pieces;
 };
-TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_work) {
+TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_work, const void* scratch,
+                   int64_t scratch_bytes) {
     constexpr int64_t kMinPieceTiles = 8;
     TailPlan none{(uint32_t)n_work, 1};
     const int64_t slots = partial_slots(k);
-    if (slots <= 0 || !p.partial_scratch) return none;
+    if (slots <= 0 || !scratch) return none;
     const int64_t tail = n_work % slots;
     if (tail == 0) return none;
     const int64_t split_keys = ((int64_t)p.max_seqlen_k + p.split_kv - 1) / p.split_kv;
     const int64_t tiles = (split_keys + 63) / 64;
     const int64_t pieces = std::min({slots / tail, tiles / kMinPieceTiles, (int64_t)sk::kMaxPieces});
     if (pieces < 2) return none;
-    if (piece_scratch_bytes(tail * pieces, k.m_per_block, p.head_dim_v) > p.partial_scratch_bytes) return none;
+    if (piece_scratch_bytes(tail * pieces, k.m_per_block, p.head_dim_v) > scratch_bytes) return none;
     return TailPlan{(uint32_t)(n_work - tail), (int)pieces};
 }
 
@@ -315,8 +316,11 @@ sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stre
     return hip_status(sk::launch_counts(a, p->batch, (hipStream_t)stream), "counts kernel launch");
 }
 
-sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v, float* o_part,
-                          float* lse_part, void* stream) {
+// sk_attn_partial with the load-balance scratch given explicitly (NULL: every
+// item runs whole).  `noalloc`: the scratch is the library's own, and a
+// problem whose worst-case piece scratch exceeds it is rejected.
+static sk_status partial_impl(const sk_problem* p, const void* q, const void* k, const void* v, float* o_part,
+                              float* lse_part, void* stream, bool noalloc) {
     sk_status st = check_problem(p);
     if (st != SK_OK) return st;
     const sk_problem rp = resolved(*p);
@@ -367,19 +371,47 @@ sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, con
     a.n_work = (uint32_t)n_work;
     a.scale = p->softmax_scale;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-    if (p->partial_scratch && !aligned(p->partial_scratch, 16))
+    void* scratch = p->partial_scratch;
+    int64_t scratch_bytes = p->partial_scratch_bytes;
+    if (noalloc) {
+        const int64_t slots = partial_slots(kern);
+        const int64_t need = slots > 0 ? piece_scratch_bytes(slots, kern.m_per_block, p->head_dim_v) : 0;
+        if (need > sk::kStaticScratchBytes)
+            return fail(SK_ERR_UNSUPPORTED,
+                        "sk_attn_partial_noalloc: this problem's load balance needs %lld bytes of scratch, above "
+                        "the library's %lld",
+                        (long long)need, (long long)sk::kStaticScratchBytes);
+        scratch = nullptr;
+        scratch_bytes = 0;
+        if (need > 0) {
+            const hipError_t e = sk::static_scratch(&scratch);
+            if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+            scratch_bytes = sk::kStaticScratchBytes;
+        }
+    } else if (scratch && !aligned(scratch, 16)) {
         return fail(SK_ERR_INVALID_ARG, "partial_scratch must be 16-byte aligned");
-    const TailPlan plan = plan_tail(*p, kern, n_work);
+    }
+    const TailPlan plan = plan_tail(*p, kern, n_work, scratch, scratch_bytes);
     a.n_main = plan.n_main;
     a.pieces = plan.pieces;
     a.piece_o = nullptr;
     a.piece_l = nullptr;
     if (plan.pieces > 1) {
         const int64_t piece_rows = (n_work - plan.n_main) * (int64_t)plan.pieces * kern.m_per_block;
-        a.piece_o = static_cast<float*>(p->partial_scratch);
+        a.piece_o = static_cast<float*>(scratch);
         a.piece_l = a.piece_o + piece_rows * p->head_dim_v;
     }
     return hip_status(kern.launch(a, (hipStream_t)stream), "partial kernel launch");
+}
+
+sk_status sk_attn_partial(const sk_problem* p, const void* q, const void* k, const void* v, float* o_part,
+                          float* lse_part, void* stream) {
+    return partial_impl(p, q, k, v, o_part, lse_part, stream, false);
+}
+
+sk_status sk_attn_partial_noalloc(const sk_problem* p, const void* q, const void* k, const void* v, float* o_part,
+                                  float* lse_part, void* stream) {
+    return partial_impl(p, q, k, v, o_part, lse_part, stream, true);
 }
 
 sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float* lse_part, const int32_t* counts,
