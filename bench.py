@@ -33,7 +33,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_hbm_traffic.json")
 # the partial entry point's kernels and the host code that plans their launch
-PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/mfma_common.hpp",
+PARTIAL_SOURCES = ["split_kv_attention_amd/csrc/partial_bf16.hip", "split_kv_attention_amd/csrc/pieces.hpp",
+                   "split_kv_attention_amd/csrc/mfma_common.hpp",
                    "split_kv_attention_amd/csrc/sk_common.hpp", "split_kv_attention_amd/csrc/splitkv_api.cpp"]
 
 
@@ -63,10 +64,11 @@ def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> d
     """Write the traffic file (TRAFFIC_FILE unless `path` is given) from two
     rocprofv3 counter runs of this script with --copy-check: `--pmc
     FETCH_SIZE` into fetch_dir and `--pmc WRITE_SIZE` into write_dir (csv
-    output, file prefix "run").  Each counter is averaged over the partial
-    kernel's and the piece merge's dispatches and scaled by what it reads
-    for the plain 1 GiB device copy (the largest dispatch that is not one of
-    this library's kernels)."""
+    output, file prefix "run").  Each counter is averaged over the split
+    launches of the partial kernel (those followed by their piece merge; the
+    unsplit comparison's launches have no pieces) and the piece merge's
+    dispatches, and scaled by what it reads for the plain 1 GiB device copy
+    (the largest dispatch that is not one of this library's kernels)."""
     import csv
     from collections import defaultdict
 
@@ -87,7 +89,13 @@ def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> d
         other = []
         for i, v in vals.items():
             key = next((k for k in mine if k in names[i]), None)
-            if key:
+            if key == "partial_bf16_kernel":
+                # the split-3 launches only: each is followed by its piece
+                # merge (the unsplit comparison's launches have no pieces)
+                nxt = str(int(i) + 1)
+                if nxt in names and "merge_pieces_kernel" in names[nxt]:
+                    mine[key].append(v)
+            elif key:
                 mine[key].append(v)
             elif "sk::" not in names[i] and "_ZN2sk" not in names[i]:
                 other.append(v)
@@ -107,7 +115,7 @@ def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> d
     H, Sq, Sk, S = w.heads, w.sq[0], w.sk[0], w.split_kv
     algorithmic = Sq * H * w.d_qk * 2 + Sk * H * (w.d_qk + w.d_v) * 2 + S * H * Sq * (w.d_v + 1) * 4
     out = {
-        "kernel": "sk_attn_partial: partial_bf16_kernel<192,128> + merge_pieces_kernel<128>",
+        "kernel": "sk_attn_partial: partial_bf16_kernel<192,128> + merge_pieces_kernel<128,128>",
         "workload": w.name,
         "kernel_source_sha256": kernel_source_hash(),
         "kernel_sources": PARTIAL_SOURCES,
@@ -153,12 +161,12 @@ def visible_pairs(w) -> int:
     return total
 
 
-def sweep() -> None:
-    """Every workload of the parity suite through counts -> partial ->
-    combine, medians of HIP-event timings on one stream; one JSON line per
-    workload with the partial's rate against its roofline (bf16 MFMA or
-    HBM, whichever bounds it; the f32 kernel against the fp32 vector peak)
-    and the combine's against HBM."""
+def sweep(only: str | None = None) -> None:
+    """Every workload of the parity suite (or those whose name starts with
+    `only`) through counts -> partial -> combine, medians of HIP-event
+    timings on one stream; one JSON line per workload with the partial's
+    rate against its roofline (bf16 MFMA or HBM, whichever bounds it; the f32
+    kernel against the fp32 vector peak) and the combine's against HBM."""
     import numpy as np
     import torch
 
@@ -166,6 +174,8 @@ def sweep() -> None:
 
     torch.cuda.set_device(0)
     for w in workloads.CONFIGS:
+        if only and not w.name.startswith(only):
+            continue
         inputs = workloads.make_inputs(w, "cuda:0", seed=3)
         prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
         counts, o_part, lse_part, out, lse_out = attention.alloc_outputs(prob, inputs["q"], inputs["v"])
@@ -435,6 +445,7 @@ def main() -> int:
     ap.add_argument("--backward-steps", type=int, default=10, help="timed backward calls (0: skip)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--only", default=None, help="with --sweep: only workloads whose name starts with this")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload of the parity suite (one JSON line each), then exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -448,7 +459,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
     if args.sweep:
-        sweep()
+        sweep(args.only)
         return 0
 
     import torch
@@ -506,9 +517,23 @@ def main() -> int:
         _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, sh)
         b.record(stream)
         cold.append((a, b))
+    # The same bracket around a kernel that does almost nothing (a 64-float
+    # fill) after the same flush: the fixed cost every cold event-timed
+    # launch pays (dispatch, start-up, completion), reported beside the
+    # combine's time.
+    tiny = torch.empty(64, dtype=torch.float32, device=dev)
+    floor = []
+    for _ in range(args.cold_iters):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        tiny.fill_(1.0)
+        b.record(stream)
+        floor.append((a, b))
     torch.cuda.synchronize()
     t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
-    del flush
+    t_launch_floor = sorted(x.elapsed_time(y) for x, y in floor)[len(floor) // 2]
+    del flush, tiny
 
     unsplit = time_unsplit(w, inputs, stream, args.steps, t_partial, t_combine, args.warmup)
 
@@ -558,7 +583,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "sk_attn_partial (partial_bf16_kernel<192,128>, then merge_pieces_kernel<128> for the "
+            "kernel": "sk_attn_partial (partial_bf16_kernel<192,128>, then merge_pieces_kernel<128,128> for the "
                       "last round's key pieces)",
             "kernel_ms": t_partial,
             "algorithmic_flop": flops,
@@ -574,6 +599,7 @@ def main() -> int:
             "frac_cold_cache": combine_bytes / (t_combine_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "frac_in_pipeline": combine_bytes / (t_combine * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "peak": PEAK_HBM_GBPS,
+            "ms_cold_launch_floor": t_launch_floor,
         },
         "counts_ms": t_counts,
         "unsplit": unsplit,

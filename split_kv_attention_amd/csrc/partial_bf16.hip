@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "mfma_common.hpp"
+#include "pieces.hpp"
 #include "sk_common.hpp"
 
 namespace sk {
@@ -97,8 +98,8 @@ void partial_bf16_kernel(PartialArgs a) {
 
     // The block's key range for this split, from its last row.  A split
     // with no key for the whole block exits without writing anything: its
-    // slots are never read (the combine merges only the block's populated
-    // splits).
+    // slots take no part in the merge (the combine merges only the block's
+    // populated splits).
     int ks, ke;
     block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kBM, sq.sq) - 1, it.split, ks, ke);
     if (ks >= ke) return;
@@ -507,76 +508,13 @@ void partial_bf16_kernel(PartialArgs a) {
     if (half == 0) *lp = empty ? -INFINITY : m_i * a.scale + logf(l_tot);
 }
 
-// Merge of the pieces of each tail item into its o_part /
-// lse_part slot: the pieces are a partition of the split's keys, so this is
-// the same log-sum-exp merge as the combine (rocmlirTriton page, "NaN-safe
-// merge"): m = max(max_p L_p, lowest finite), w_p = exp(L_p - m),
-// O_s = sum_p w_p O_p / max(sum_p w_p, 1), L_s = m + log(sum_p w_p), and a
-// row no piece saw any key of keeps (0, -inf).
-// One thread per (row, 4 values) of a tail item; a block covers
-// kThreads / (DV / 4) rows of one item.  All pieces of a row are loaded
-// before any is used.
-template <int DV>
-__global__ __launch_bounds__(kThreads) void merge_pieces_kernel(PartialArgs a) {
-    constexpr int kParts = DV / 4;
-    constexpr int kRows = kThreads / kParts;  // rows per block
-    constexpr int kBlocks = kBM / kRows;      // blocks per item
-    const uint32_t tail_i = blockIdx.x / kBlocks;
-    const int r = (int)(blockIdx.x % kBlocks) * kRows + (int)threadIdx.x / kParts;
-    const int part = (int)threadIdx.x % kParts;
-    const WorkItem it = decode_work(a, a.n_main + tail_i);
-    const Seq sq = load_seq(a.seqs, it.batch);
-    if (it.split >= sq.splits) return;
-    const int r0 = it.tile * kBM;
-    if (r0 + r >= sq.sq) return;
-    int ks, ke;  // a block-empty split: no piece ran, nothing is written
-    block_split_range(sq, a.seqs.mask, a.seqs.n_per_block, min(r0 + kBM, sq.sq) - 1, it.split, ks, ke);
-    if (ks >= ke) return;
-    const int64_t prow = sq.row0 + r0 + r;
-    if (prow >= a.rows) return;
-    const int P = a.pieces;
-    const int64_t base = (int64_t)tail_i * P * kBM + r;  // piece p: row base + p * kBM
-    float L[kMaxPieces];
-    float4 O[kMaxPieces];
-#pragma unroll
-    for (int p = 0; p < kMaxPieces; ++p) {
-        if (p < P) {
-            L[p] = a.piece_l[base + (int64_t)p * kBM];
-            O[p] = *reinterpret_cast<const float4*>(a.piece_o + (base + (int64_t)p * kBM) * DV + part * 4);
-        }
-    }
-    float m = -FLT_MAX;
-#pragma unroll
-    for (int p = 0; p < kMaxPieces; ++p)
-        if (p < P) m = fmaxf(m, L[p]);
-    float den = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int p = 0; p < kMaxPieces; ++p) {
-        if (p < P) {
-            const float w = expf(L[p] - m);
-            den += w;
-            acc.x = fmaf(w, O[p].x, acc.x);
-            acc.y = fmaf(w, O[p].y, acc.y);
-            acc.z = fmaf(w, O[p].z, acc.z);
-            acc.w = fmaf(w, O[p].w, acc.w);
-        }
-    }
-    const float inv = 1.0f / fmaxf(den, 1.0f);
-    const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
-    *reinterpret_cast<float4*>(a.o_part + slot * DV + part * 4) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (part == 0) a.lse_part[slot] = den > 0.f ? m + logf(den) : -INFINITY;
-}
-
 template <typename T, int DQK, int DV>
 hipError_t launch(const PartialArgs& a, hipStream_t stream) {
     const uint32_t n_tail = a.n_work - a.n_main;
     const uint32_t grid = a.n_main + n_tail * (uint32_t)a.pieces;
     hipLaunchKernelGGL((partial_bf16_kernel<T, DQK, DV>), dim3(grid), dim3(kThreads), 0, stream, a);
     if (n_tail > 0) {
-        constexpr int kBlocks = kBM / (kThreads / (DV / 4));
-        hipLaunchKernelGGL((merge_pieces_kernel<DV>), dim3(n_tail * kBlocks), dim3(kThreads), 0, stream, a);
+        launch_merge_pieces<kBM, DV>(a, n_tail, stream);
     }
     return hipGetLastError();
 }
