@@ -31,16 +31,18 @@ def _write(d, counter, rows):
 def test_write_traffic_scales_by_the_copy(tmp_path):
     bench = _bench()
     part = "_ZN2sk12_GLOBAL__N_119partial_bf16_kernelIDF16bLi192ELi128EEEvNS_11PartialArgsE"
-    merge = "void sk::(anonymous namespace)::merge_pieces_kernel<128>(sk::PartialArgs)"
+    merge = "void sk::merge_pieces_kernel<128, 128>(sk::PartialArgs)"
     comb = "_ZN2sk14combine_kernelIDF16bLi4ELb1EEEvNS_11CombineArgsE"
     copy = "__amd_rocclr_copyBuffer"
     fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
-    # two dispatches of the partial kernel (mean 300 KiB), one merge, a
-    # larger combine that must not count, and the copy read as half its size
-    _write(fetch, "FETCH_SIZE", [(part, [100.0, 150.0]), (part, [200.0, 150.0]), (merge, [10.0]),
-                                 (comb, [5e5]), (copy, [262144.0, 262144.0])])
-    _write(write, "WRITE_SIZE", [(part, [40.0]), (part, [60.0]), (merge, [4.0]), (comb, [7e5]),
-                                 (copy, [1048576.0]), ("zero_fill", [1048576.0])])
+    # two split launches of the partial kernel, each followed by its piece
+    # merge (partial mean 300 KiB, merge 10), a larger combine that must not
+    # count, an unsplit launch (no merge after it) that must not count, and
+    # the copy read as half its size
+    _write(fetch, "FETCH_SIZE", [(part, [100.0, 150.0]), (merge, [10.0]), (part, [200.0, 150.0]), (merge, [10.0]),
+                                 (comb, [5e5]), (part, [9e5]), (comb, [5e5]), (copy, [262144.0, 262144.0])])
+    _write(write, "WRITE_SIZE", [(part, [40.0]), (merge, [4.0]), (part, [60.0]), (merge, [4.0]), (comb, [7e5]),
+                                 (part, [9e5]), (comb, [7e5]), (copy, [1048576.0]), ("zero_fill", [1048576.0])])
     out = bench.write_traffic(fetch, write, path=str(tmp_path / "t.json"))
     assert out["fetch_size_kib_per_dispatch"] == {"partial_bf16_kernel": 300.0, "merge_pieces_kernel": 10.0}
     assert out["write_size_kib_per_dispatch"] == {"partial_bf16_kernel": 50.0, "merge_pieces_kernel": 4.0}
@@ -88,3 +90,23 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_runs_every_unit_on_a_pool():
+    """The pooled oracle baseline covers every (sequence, head, 32-row) unit
+    of a small packed workload and reports its pool and host."""
+    import dataclasses
+    import sys
+
+    sys.path.insert(0, ROOT)
+    from split_kv_attention_amd import workloads
+
+    bench = _bench()
+    w = dataclasses.replace(workloads.LONG_PREFILL, name="small", heads=2, sq=(70,), sk=(300,))
+    inputs = workloads.make_inputs(w, "cpu", seed=1)
+    r = bench.cpu_baseline(w, inputs, 128, budget_s=120.0, max_workers=2)
+    assert r["units_total"] == 2 * 3 and r["units_done"] == r["units_total"]
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] == min(len(os.sched_getaffinity(0)), 2)
+    for key in ("cpu_model", "numpy", "blas", "affinity_cpus", "sample"):
+        assert r[key], key
