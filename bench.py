@@ -161,12 +161,14 @@ def visible_pairs(w) -> int:
     return total
 
 
-def sweep(only: str | None = None) -> None:
+def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
     """Every workload of the parity suite (or those whose name starts with
     `only`) through counts -> partial -> combine, medians of HIP-event
     timings on one stream; one JSON line per workload with the partial's
     rate against its roofline (bf16 MFMA or HBM, whichever bounds it; the f32
-    kernel against the fp32 vector peak) and the combine's against HBM."""
+    kernel against the fp32 vector peak) and the combine's against HBM.
+    With oracle_budget_s > 0 the line also holds the oracle timed on the
+    host's cores over the same workload (cpu_baseline, that budget each)."""
     import numpy as np
     import torch
 
@@ -223,13 +225,18 @@ def sweep(only: str | None = None) -> None:
         else:
             bound, peak, unit, achieved = "hbm", PEAK_HBM_GBPS, "GB/s", part_bytes / (t_part * 1e-3) / 1e9
         comb_gbps = comb_bytes / (t_comb * 1e-3) / 1e9
-        print(json.dumps({
+        line = {
             "workload": w.name, "calls": n,
             "partial": {"ms": t_part, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                         "frac": achieved / peak, "flop": flop, "algorithmic_bytes": part_bytes},
             "combine": {"ms": t_comb, "gbps": comb_gbps, "frac": comb_gbps / PEAK_HBM_GBPS,
                         "algorithmic_bytes": comb_bytes},
-        }), flush=True)
+        }
+        if oracle_budget_s > 0:
+            base = cpu_baseline(w, inputs, prob.m_per_block, budget_s=oracle_budget_s)
+            base["gpu_speedup"] = (flop / ((t_part + t_comb) * 1e-3) / 1e12) / base["value"]
+            line["cpu_baseline"] = base
+        print(json.dumps(line), flush=True)
         del inputs, prob, counts, o_part, lse_part, out, lse_out, q, k, v
         torch.cuda.empty_cache()
 
@@ -255,7 +262,25 @@ def _blas_info() -> str:
         return "unknown"
 
 
-def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_workers: int = 16):
+def _visible_pairs_rows(w, b: int, rows) -> int:
+    """Visible (query, key) pairs of `rows` of sequence b, per head (the rule
+    of visible_pairs)."""
+    import numpy as np
+
+    sk = w.sk[b]
+    lv = w.last_valid_per_seq[b] if w.last_valid_per_seq else w.last_valid_kv_index
+    lv = sk - 1 if lv < 0 else min(lv, sk - 1)
+    q = np.asarray(rows, dtype=np.int64)
+    if w.mask == "none":
+        last = np.full(len(q), lv, dtype=np.int64)
+    else:
+        off = 0 if w.mask == "causal" else (w.prefix_offset_per_seq[b] if w.prefix_offset_per_seq else w.prefix_offset)
+        last = np.minimum(q + off, lv)
+    return int(np.clip(last + 1, 0, sk).sum())
+
+
+def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_workers: int = 16,
+                 max_host_bytes: float = 4e9):
     """The oracle (as it stands) timed on the host's cores over the whole
     workload: units of (sequence, head, 32 query rows), each the full split
     method (counts, partials at the kernel's query block, merge) against all
@@ -263,7 +288,9 @@ def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_worker
     worker and as many workers as the process may use (its CPU affinity,
     capped at the GPU's 16-core share).  Units run in a seeded random order;
     if the wall-clock budget runs out first, the finished units are the
-    sample and the rate is scaled from them."""
+    sample and the rate is scaled from them.  The inputs are copied to the
+    host before the clock starts; a workload whose K and V exceed
+    max_host_bytes is sampled by whole sequences (seeded) to fit."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor, wait, FIRST_COMPLETED
     from threadpoolctl import threadpool_limits
@@ -272,17 +299,37 @@ def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_worker
 
     affinity = len(os.sched_getaffinity(0))
     workers = max(1, min(affinity, max_workers))
-    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in inputs.items()}
+    nseq = len(w.sq)
+    per_seq = [w.heads * w.sk[b] * (w.d_qk + w.d_v) * inputs["k"].element_size() for b in range(nseq)]
+    seqs = list(range(nseq))
+    if sum(per_seq) > max_host_bytes:
+        keep, tot = [], 0.0
+        for b in np.random.default_rng(1).permutation(nseq):
+            if tot + per_seq[b] <= max_host_bytes or not keep:
+                keep.append(int(b))
+                tot += per_seq[b]
+        seqs = sorted(keep)
+    if len(seqs) == nseq:
+        host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in inputs.items()}
+    else:
+        # dense batch [B, H, S, D]: only the kept sequences, indexed [b, h, ...]
+        host = {}
+        for k, v in inputs.items():
+            if hasattr(v, "cpu") and v.dim() == 4:
+                host[k] = _HostSequences({b: v[b].cpu() for b in seqs})
+            else:
+                host[k] = v.cpu() if hasattr(v, "cpu") else v
     chunk = 32
-    units = [(b, h, r0) for b in range(len(w.sq)) for h in range(w.heads) for r0 in range(0, w.sq[b], chunk)]
+    units = [(b, h, r0) for b in seqs for h in range(w.heads) for r0 in range(0, w.sq[b], chunk)]
+    units_total = sum(w.heads * ((w.sq[b] + chunk - 1) // chunk) for b in range(nseq))
     order = np.random.default_rng(0).permutation(len(units))
 
     def run_unit(i):
         b, h, r0 = units[i]
         rows = np.arange(r0, min(r0 + chunk, w.sq[b]))
         adapter.expected(w, host, m_per_block, rows_per_seq={bb: (rows if bb == b else rows[:0])
-                                                              for bb in range(len(w.sq))}, heads=[h])
-        return float(len(rows)) * w.sk[b]  # (query, key) pairs, every key visible (no mask)
+                                                              for bb in range(nseq)}, heads=[h])
+        return float(_visible_pairs_rows(w, b, rows))
 
     pairs = 0.0
     done = 0
@@ -306,23 +353,36 @@ def cpu_baseline(w, inputs, m_per_block: int, budget_s: float = 45.0, max_worker
                         pending.add(ex.submit(run_unit, int(i)))
     dt = time.perf_counter() - t0
     flops = 2.0 * (w.d_qk + w.d_v) * pairs
-    full = done == len(units)
-    what = "the whole workload" if full else f"{done} of {len(units)} units (seeded random order; budget {budget_s:.0f} s)"
+    full = done == units_total
+    what = "the whole workload" if full else \
+        f"{done} of {units_total} units (seeded random order; budget {budget_s:.0f} s" + \
+        (f"; {len(seqs)} of {nseq} sequences on the host)" if len(seqs) < nseq else ")")
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{what}: units of (sequence, head, {chunk} query rows) x all {w.sk[0]} keys, full split method "
-                  f"in f64, {dt:.1f} s wall on a {workers}-thread pool, one BLAS thread each",
+        "sample": f"{what}: units of (sequence, head, {chunk} query rows) x all the sequence's keys, full split "
+                  f"method in f64, {dt:.1f} s wall on a {workers}-thread pool, one BLAS thread each",
         "seconds": dt,
         "units_done": done,
-        "units_total": len(units),
+        "units_total": units_total,
         "cpu_model": _cpu_model(),
         "affinity_cpus": affinity,
         "numpy": np.__version__,
         "blas": _blas_info(),
     }
+
+
+class _HostSequences:
+    """Some sequences of a dense [B, H, S, D] batch on the host, indexed like
+    the batch by [b, h, ...] (only the kept b)."""
+
+    def __init__(self, per_seq):
+        self.per_seq = per_seq
+
+    def __getitem__(self, key):
+        return self.per_seq[key[0]][key[1:]]
 
 
 def time_unsplit(w, inputs, stream, steps: int, t_partial_split: float, t_combine_split: float, warmup: int):
@@ -446,6 +506,8 @@ def main() -> int:
     ap.add_argument("--copy-check", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--only", default=None, help="with --sweep: only workloads whose name starts with this")
+    ap.add_argument("--oracle-seconds", type=float, default=0.0,
+                    help="with --sweep: also time the oracle on the host for up to this many seconds per workload")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload of the parity suite (one JSON line each), then exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -459,7 +521,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
     if args.sweep:
-        sweep(args.only)
+        sweep(args.only, args.oracle_seconds)
         return 0
 
     import torch

@@ -110,3 +110,22 @@ def test_cpu_baseline_runs_every_unit_on_a_pool():
     assert r["cores"] == min(len(os.sched_getaffinity(0)), 2)
     for key in ("cpu_model", "numpy", "blas", "affinity_cpus", "sample"):
         assert r[key], key
+
+
+def test_cpu_baseline_samples_whole_sequences_of_a_large_dense_batch():
+    """Past the host-memory cap the baseline keeps whole sequences (seeded)
+    and reports the sample against the whole workload's units."""
+    import dataclasses
+    import sys
+
+    sys.path.insert(0, ROOT)
+    from split_kv_attention_amd import workloads
+
+    bench = _bench()
+    w = dataclasses.replace(workloads.DECODE_BF16, name="small_decode", heads=2, sq=(1,) * 6, sk=(200,) * 6)
+    inputs = workloads.make_inputs(w, "cpu", seed=2)
+    one_seq = w.heads * 200 * (w.d_qk + w.d_v) * 2
+    r = bench.cpu_baseline(w, inputs, 128, budget_s=120.0, max_workers=2, max_host_bytes=2.5 * one_seq)
+    assert r["units_total"] == 6 * 2
+    assert r["units_done"] == 2 * 2  # two whole sequences fit under the cap
+    assert "2 of 6 sequences" in r["sample"]
