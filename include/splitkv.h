@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SK_ABI_VERSION 5
+#define SK_ABI_VERSION 6
 
 typedef enum sk_status {
     SK_OK = 0,
@@ -275,6 +275,25 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
  * (f32 D per (head, row) and one f32 dQ sum per (head, S_dq split, row, dim);
  * S_dq depends on the device's CU count), or -1 if `p` is invalid. */
 int64_t sk_backward_workspace_bytes(const sk_problem* p);
+
+/* Bounds-check report of a checked build of the library (compiled with
+ * SK_CHECKED=1: split_kv_attention_amd.build.build_checked).  Its forward
+ * kernels (counts, partial, piece merge, combine) test every global index
+ * they derive from the problem and the device-side tables against the
+ * logical extent it addresses, and skip the access when it falls outside
+ * (a Q row reads as zeros; the other sites end the thread's work item).
+ * Sites: 1 work item (batch, head, split), 2 Q row (against total_q),
+ * 3 last key row of a partial's key range (against cu_seqlens_k[batch], or
+ * max_seqlen_k for dense K/V), 4 o_part / lse_part slot, 5 key-piece
+ * scratch slot, 6 counts entry, 7 combine row (head, sequence), 8 combine
+ * split slot (against split_kv).  Returns the number of failed tests on the
+ * current device since the previous call (each thread counts its own) and
+ * resets it; the first one's site, index and limit go to the three pointers
+ * (each may be NULL).  It synchronises with the device (blocking copies),
+ * so call it after the work it reports on has finished.  A normal build
+ * returns -1 with SK_ERR_UNSUPPORTED in sk_last_error; -1 with SK_ERR_HIP
+ * if the record cannot be read. */
+int64_t sk_check_violations(int64_t* first_site, int64_t* first_index, int64_t* first_limit);
 
 #ifdef __cplusplus
 }

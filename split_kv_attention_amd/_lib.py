@@ -35,6 +35,7 @@ EXPORTS = (
     "sk_attn_combine",
     "sk_attn_backward",
     "sk_backward_workspace_bytes",
+    "sk_check_violations",
 )
 
 
@@ -132,6 +133,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sk_attn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
     lib.sk_backward_workspace_bytes.restype = ctypes.c_int64
     lib.sk_backward_workspace_bytes.argtypes = [P]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.sk_check_violations.restype = ctypes.c_int64
+    lib.sk_check_violations.argtypes = [i64p, i64p, i64p]
     if path is None:
         _lib = lib
     return lib
@@ -246,6 +250,17 @@ def sk_backward_workspace_bytes(problem: SkProblem) -> int:
     if n < 0:
         raise SplitKVError(SK_ERR_INVALID_ARG, sk_last_error())
     return n
+
+
+def sk_check_violations(lib: ctypes.CDLL | None = None):
+    """(count, first site, first index, first limit) of a bounds-checked
+    build (`lib`, default the loaded library); raises for a normal build."""
+    lib = lib or load()
+    site, index, limit = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    n = lib.sk_check_violations(ctypes.byref(site), ctypes.byref(index), ctypes.byref(limit))
+    if n < 0:
+        raise SplitKVError(SK_ERR_UNSUPPORTED, lib.sk_last_error().decode())
+    return n, site.value, index.value, limit.value
 
 
 def sk_attn_backward(problem: SkProblem, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes: int,

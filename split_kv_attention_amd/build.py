@@ -4,7 +4,9 @@ Every call recompiles: each translation unit under csrc/ goes to an object
 file in _build/, then they are linked into split_kv_attention_amd/libsplitkv.so.
 Usage:  python -m split_kv_attention_amd.build   (or __graft_entry__.build()).
 
-build_asan() makes a second copy of the library whose HOST code is built with
+build_checked() makes libsplitkv_checked.so, whose forward kernels guard every
+global index (compile flag SK_CHECKED, reported by sk_check_violations).
+build_asan() makes a copy of the library whose HOST code is built with
 AddressSanitizer (device code unchanged) in _build/asan/; a process that loads
 it must preload the sanitizer runtime (asan_runtime()).  It exists for the
 host-side tests of argument checking and dispatch.
@@ -63,19 +65,24 @@ def _compile(src: str, extra: list[str], out_dir: str = BUILD) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source and link libsplitkv.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra_flags or [])
+def _build_lib(path: str, flags: list[str], out_dir: str) -> str:
+    """Compile every source with `flags` into out_dir and link `path`."""
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, flags, out_dir), srcs))
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+    return path
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile every source and link libsplitkv.so; returns the library path."""
+    _build_lib(LIB_PATH, list(extra_flags or []), BUILD)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH
@@ -103,17 +110,19 @@ def build_asan() -> str:
     """Compile every source with the host pass under AddressSanitizer and link
     _build/asan/libsplitkv_asan.so; returns its path.  The shared library
     leaves the sanitizer's symbols to the preloaded runtime."""
-    os.makedirs(ASAN_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, ASAN_HOST_FLAGS, ASAN_DIR), srcs))
-    tmp = ASAN_LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, ASAN_LIB_PATH)
-    return ASAN_LIB_PATH
+    return _build_lib(ASAN_LIB_PATH, ASAN_HOST_FLAGS, ASAN_DIR)
+
+
+CHECKED_LIB_PATH = os.path.join(PKG, "libsplitkv_checked.so")
+
+
+def build_checked() -> str:
+    """Compile every source with -DSK_CHECKED=1 (the forward kernels test
+    every global index they derive and count the failures, which
+    sk_check_violations reports) and link
+    split_kv_attention_amd/libsplitkv_checked.so beside the normal library;
+    returns its path."""
+    return _build_lib(CHECKED_LIB_PATH, ["-DSK_CHECKED=1"], os.path.join(BUILD, "checked"))
 
 
 if __name__ == "__main__":

@@ -117,10 +117,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         b = (int)(rr / a.seqs.max_sq);
         r = (int)(rr - (int64_t)b * a.seqs.max_sq);
     }
+    if (!in_bounds(a.check, kSiteCombineRow, h, a.heads) || !in_bounds(a.check, kSiteCombineRow, b, a.batch)) return;
     const Seq s = load_seq(a.seqs, b);
     if (r >= s.sq) return;
     const int64_t row = s.row0 + r;
     if (row >= a.rows) return;
+    if (!in_bounds(a.check, kSiteCombineSplit, s.splits - 1, a.seqs.s_max)) return;
 
     // Every slot s < S_b was written by the partial kernel, so the first
     // chunk's loads are issued together, before the count is known; splits

@@ -9,6 +9,7 @@ __global__ __launch_bounds__(256) void counts_kernel(CountsArgs a) {
     const Seq s = load_seq(a.seqs, blockIdx.y);
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= s.sq || s.row0 + r >= a.rows) return;
+    if (!in_bounds(a.check, kSiteCountsRow, s.row0 + r, a.rows)) return;
     a.counts[s.row0 + r] = valid_split_count(s, a.seqs.mask, a.seqs.n_per_block, r);
 }
 

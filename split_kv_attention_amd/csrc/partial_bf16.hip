@@ -90,6 +90,9 @@ void partial_bf16_kernel(PartialArgs a) {
         item = a.n_main + tail_i;
     }
     const WorkItem it = decode_work(a, item);
+    if (!in_bounds(a.check, kSiteWorkItem, it.batch, a.batch) || !in_bounds(a.check, kSiteWorkItem, it.head, a.heads) ||
+        !in_bounds(a.check, kSiteWorkItem, it.split, a.seqs.s_max))
+        return;
     const Seq sq = load_seq(a.seqs, it.batch);
     if (it.split >= sq.splits) return;
     const int r0 = it.tile * kBM;
@@ -103,6 +106,9 @@ void partial_bf16_kernel(PartialArgs a) {
     int ks, ke;
     block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kBM, sq.sq) - 1, it.split, ks, ke);
     if (ks >= ke) return;
+    if (!in_bounds(a.check, kSiteKeys, (sq.krow0 >= 0 ? sq.krow0 : 0) + ke - 1,
+                   sq.krow0 >= 0 ? total_keys(a.seqs, a.batch) : (int64_t)a.seqs.max_sk))
+        return;
     if (piece >= 0) {
         // piece p of P takes key tiles [nt p / P, nt (p + 1) / P) of the split
         const int nt = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
@@ -128,6 +134,9 @@ void partial_bf16_kernel(PartialArgs a) {
     const int half = lane >> 5;  // which 8-wide k slice / which 4 accumulator rows
     const int qrow = r0 + wave * 32 + col;
     const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
+    const bool q_ok = row_ok && in_bounds(a.check, kSiteQRow,
+                                          a.seqs.cu_q ? sq.row0 + qrow : (int64_t)it.batch * a.seqs.max_sq + qrow,
+                                          a.rows);
     const bool wave_active = (r0 + wave * 32) < sq.sq;
     // Visibility limits of this lane's row, clamped into int range (keys are int).
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
@@ -149,7 +158,7 @@ void partial_bf16_kernel(PartialArgs a) {
                              (int64_t)it.head * a.q_head + half * 8;
 #pragma unroll
         for (int t = 0; t < DQK / 16; ++t) {
-            uint4 x = row_ok ? *reinterpret_cast<const uint4*>(qp + t * 16) : make_uint4(0, 0, 0, 0);
+            uint4 x = q_ok ? *reinterpret_cast<const uint4*>(qp + t * 16) : make_uint4(0, 0, 0, 0);
             qf[t] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -491,10 +500,12 @@ void partial_bf16_kernel(PartialArgs a) {
     float* lp;
     if (piece < 0) {
         const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+        if (!in_bounds(a.check, kSitePartialSlot, slot, (int64_t)a.heads * a.seqs.s_max * a.rows)) return;
         op = a.o_part + slot * DV;
         lp = a.lse_part + slot;
     } else {
         const int64_t slot = ((int64_t)tail_i * a.pieces + piece) * kBM + wave * 32 + col;
+        if (!in_bounds(a.check, kSitePieceSlot, slot, (int64_t)(a.n_work - a.n_main) * a.pieces * kBM)) return;
         op = a.piece_o + slot * DV;
         lp = a.piece_l + slot;
     }

@@ -45,6 +45,9 @@ __global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_k
     __shared__ float4 Vs[BN * DV / 4];
 
     const WorkItem it = decode_work(a, blockIdx.x);
+    if (!in_bounds(a.check, kSiteWorkItem, it.batch, a.batch) || !in_bounds(a.check, kSiteWorkItem, it.head, a.heads) ||
+        !in_bounds(a.check, kSiteWorkItem, it.split, a.seqs.s_max))
+        return;
     const Seq sq = load_seq(a.seqs, it.batch);
     if (it.split >= sq.splits) return;
     const int r0 = it.tile * kF32Rows;
@@ -57,6 +60,9 @@ __global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_k
     int ks, ke;
     block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kF32Rows, sq.sq) - 1, it.split, ks, ke);
     if (ks >= ke) return;
+    if (!in_bounds(a.check, kSiteKeys, (sq.krow0 >= 0 ? sq.krow0 : 0) + ke - 1,
+                   sq.krow0 >= 0 ? total_keys(a.seqs, a.batch) : (int64_t)a.seqs.max_sk))
+        return;
     // Sliding window: tiles below the first row's first visible key hold
     // nothing any row sees.
     const int64_t win = a.seqs.window_left;
@@ -69,6 +75,9 @@ __global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_k
     const int sub = tid % SUB;
     const int qrow = r0 + tid / SUB;
     const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
+    const bool q_ok = row_ok && in_bounds(a.check, kSiteQRow,
+                                          a.seqs.cu_q ? sq.row0 + qrow : (int64_t)it.batch * a.seqs.max_sq + qrow,
+                                          a.rows);
     const int64_t vis = vis_last(sq, mask, qrow);
     const int64_t lo = vis_first(sq, win, qrow);
 
@@ -83,7 +92,7 @@ __global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_k
     float qv[QS];
 #pragma unroll
     for (int d = 0; d < QS; d += 4) {
-        float4 x = row_ok ? *reinterpret_cast<const float4*>(qp + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 x = q_ok ? *reinterpret_cast<const float4*>(qp + d) : make_float4(0.f, 0.f, 0.f, 0.f);
         qv[d] = x.x;
         qv[d + 1] = x.y;
         qv[d + 2] = x.z;
@@ -169,6 +178,7 @@ __global__ __launch_bounds__((kF32Rows * f32_sub<DQK, DV>())) void partial_f32_k
     const bool empty = (m == -INFINITY);
     const float inv = empty ? 0.f : 1.0f / l;
     const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+    if (!in_bounds(a.check, kSitePartialSlot, slot, (int64_t)a.heads * a.seqs.s_max * a.rows)) return;
     float* op = a.o_part + slot * DV + sub * VS;
 #pragma unroll
     for (int d = 0; d < VS; d += 4)

@@ -37,6 +37,8 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(PartialArgs a) {
     if (prow >= a.rows) return;
     const int P = a.pieces;
     const int64_t base = (int64_t)tail_i * P * BM + r;  // piece p: row base + p * BM
+    if (!in_bounds(a.check, kSitePieceSlot, base + (int64_t)(P - 1) * BM, (int64_t)(a.n_work - a.n_main) * P * BM))
+        return;
     float L[kMaxPieces];
     float4 O[kMaxPieces];
 #pragma unroll
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(PartialArgs a) {
     }
     const float inv = 1.0f / fmaxf(den, 1.0f);
     const int64_t slot = ((int64_t)it.head * a.seqs.s_max + it.split) * a.rows + prow;
+    if (!in_bounds(a.check, kSitePartialSlot, slot, (int64_t)a.heads * a.seqs.s_max * a.rows)) return;
     *reinterpret_cast<float4*>(a.o_part + slot * DV + part * 4) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     if (part == 0) a.lse_part[slot] = den > 0.f ? m + logf(den) : -INFINITY;

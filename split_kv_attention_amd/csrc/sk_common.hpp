@@ -6,7 +6,51 @@
 
 #include "splitkv.h"
 
+#ifndef SK_CHECKED
+#define SK_CHECKED 0
+#endif
+
 namespace sk {
+
+// Bounds-checked build (compiled with -DSK_CHECKED=1, see
+// split_kv_attention_amd/build.py): every global index the forward kernels
+// derive is checked against the logical extent of the buffer it addresses
+// (rows, heads, splits, slots, keys of cu_seqlens_k).  A violation is counted,
+// the first one is recorded, and the access is skipped.  In a normal build
+// the checks compile away.
+struct CheckRecord {
+    unsigned int count;  // violations since the last report
+    unsigned int site;   // the first violation's check site (CheckSite)
+    long long index;     // its index
+    long long limit;     // the extent the index had to stay below
+};
+enum CheckSite : int {
+    kSiteWorkItem = 1,     // decoded (tile, head, split, batch) of a work item
+    kSiteQRow = 2,         // query row read by a partial kernel
+    kSiteKeys = 3,         // last key row of a partial kernel's key range
+    kSitePartialSlot = 4,  // o_part / lse_part slot written
+    kSitePieceSlot = 5,    // piece scratch slot written or read
+    kSiteCountsRow = 6,    // counts entry written
+    kSiteCombineRow = 7,   // row merged by the combine (o_part / lse_part / out / lse_out)
+    kSiteCombineSplit = 8, // split slot read by the combine
+};
+__device__ __forceinline__ bool in_bounds(CheckRecord* rec, int site, int64_t i, int64_t limit) {
+#if SK_CHECKED
+    if (i >= 0 && i < limit) return true;
+    if (rec && atomicAdd(&rec->count, 1u) == 0u) {
+        rec->site = (unsigned int)site;
+        rec->index = i;
+        rec->limit = limit;
+    }
+    return false;
+#else
+    (void)rec;
+    (void)site;
+    (void)i;
+    (void)limit;
+    return true;
+#endif
+}
 
 // Per-sequence data as the kernels see it.  Scalars are copied from
 // sk_problem; the pointers are the caller's optional device arrays.
@@ -104,6 +148,12 @@ constexpr int kMaxPieces = 16;
 // and its address on the current device (looked up once per device).
 constexpr int64_t kStaticScratchBytes = (int64_t)36 << 20;
 hipError_t static_scratch(void** out);
+// The bounds-check record on the current device (NULL in a normal build).
+hipError_t check_record(CheckRecord** out);
+// Number of keys of a packed K/V (cu_seqlens_k[batch]) or of one dense sequence.
+__device__ __forceinline__ int64_t total_keys(const SeqTable& t, int batch) {
+    return t.cu_k ? (int64_t)t.cu_k[batch] : (int64_t)t.max_sk;
+}
 
 // Key range [ks, ke) of split `split` for the query block whose last row is
 // last_row: the count formula at that row gives keys per split, split s
@@ -159,6 +209,9 @@ struct PartialArgs {
     int32_t pieces;    // 2 .. kMaxPieces when n_main < n_work
     float* piece_o;
     float* piece_l;
+    int32_t batch;       // sequences
+    int32_t pad_;
+    CheckRecord* check;  // bounds-checked build only (else NULL)
 };
 
 // Decoded work item of a partial kernel.
@@ -265,6 +318,7 @@ struct CountsArgs {
     int32_t* counts;
     SeqTable seqs;
     int64_t rows;  // length of counts: rows past it (inconsistent cu_seqlens) are not written
+    CheckRecord* check;  // bounds-checked build only (else NULL)
 };
 
 struct CombineArgs {
@@ -282,6 +336,7 @@ struct CombineArgs {
     int32_t row_blocks;  // blocks per head (set by the launcher)
     int32_t m_per_block; // query block of the partial kernel (0: unknown, no block clamp)
     int32_t pad_;
+    CheckRecord* check;  // bounds-checked build only (else NULL)
 };
 
 // Launchers (one translation unit each).

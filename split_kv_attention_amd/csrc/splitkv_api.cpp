@@ -313,6 +313,8 @@ sk_status sk_valid_split_counts(const sk_problem* p, int32_t* counts, void* stre
     a.counts = counts;
     a.seqs = seq_table(*p);
     a.rows = rows_of(*p);
+    const hipError_t ce = sk::check_record(&a.check);
+    if (ce != hipSuccess) return hip_status(ce, "bounds-check record lookup");
     return hip_status(sk::launch_counts(a, p->batch, (hipStream_t)stream), "counts kernel launch");
 }
 
@@ -401,6 +403,10 @@ static sk_status partial_impl(const sk_problem* p, const void* q, const void* k,
         a.piece_o = static_cast<float*>(scratch);
         a.piece_l = a.piece_o + piece_rows * p->head_dim_v;
     }
+    a.batch = p->batch;
+    a.pad_ = 0;
+    const hipError_t ce = sk::check_record(&a.check);
+    if (ce != hipSuccess) return hip_status(ce, "bounds-check record lookup");
     return hip_status(kern.launch(a, (hipStream_t)stream), "partial kernel launch");
 }
 
@@ -449,7 +455,37 @@ sk_status sk_attn_combine(const sk_problem* p, const float* o_part, const float*
     a.row_blocks = 0;
     a.m_per_block = pick_partial(*p).m_per_block;  // 0 when no partial kernel exists for p
     a.pad_ = 0;
+    const hipError_t ce = sk::check_record(&a.check);
+    if (ce != hipSuccess) return hip_status(ce, "bounds-check record lookup");
     return hip_status(sk::launch_combine(a, p->out_dtype, (hipStream_t)stream), "combine kernel launch");
+}
+
+int64_t sk_check_violations(int64_t* first_site, int64_t* first_index, int64_t* first_limit) {
+    sk::CheckRecord* rec = nullptr;
+    const hipError_t e = sk::check_record(&rec);
+    if (e != hipSuccess) {
+        fail(SK_ERR_HIP, "locating the bounds-check record failed: %s", hipGetErrorString(e));
+        return -1;
+    }
+    if (!rec) {
+        fail(SK_ERR_UNSUPPORTED, "not a bounds-checked build (compiled without SK_CHECKED)");
+        return -1;
+    }
+    sk::CheckRecord h{};
+    if (hipMemcpy(&h, rec, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) {
+        fail(SK_ERR_HIP, "reading the bounds-check record failed");
+        return -1;
+    }
+    const sk::CheckRecord zero{};
+    if (hipMemcpy(rec, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
+        fail(SK_ERR_HIP, "resetting the bounds-check record failed");
+        return -1;
+    }
+    if (first_site) *first_site = h.count ? (int64_t)h.site : 0;
+    if (first_index) *first_index = h.count ? (int64_t)h.index : 0;
+    if (first_limit) *first_limit = h.count ? (int64_t)h.limit : 0;
+    ok();
+    return (int64_t)h.count;
 }
 
 int64_t sk_backward_workspace_bytes(const sk_problem* p) {

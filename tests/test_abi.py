@@ -9,7 +9,7 @@ import subprocess
 import pytest
 
 import split_kv_attention_amd as sk
-from split_kv_attention_amd import _lib
+from split_kv_attention_amd import _lib, build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "splitkv.h")
@@ -244,3 +244,22 @@ def test_split_kv_error_carries_the_message():
     p.split_kv = -2
     with pytest.raises(sk.SplitKVError, match="split_kv"):
         sk.sk_valid_split_counts(p, FAKE, 0)
+
+
+def test_normal_build_has_no_bounds_check_record():
+    lib = _lib.load()
+    assert lib.sk_check_violations(None, None, None) == -1
+    assert "SK_CHECKED" in lib.sk_last_error().decode()
+    with pytest.raises(sk.SplitKVError, match="bounds-checked"):
+        _lib.sk_check_violations()
+
+
+def test_checked_build_links_and_exports_every_function():
+    lib = _lib.load(build.build_checked())
+    assert lib.sk_abi_version() == _lib.load().sk_abi_version()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # host-side argument checks are the same code in both builds
+    p = _good()
+    p.split_kv = -2
+    assert lib.sk_valid_split_counts(ctypes.byref(p), FAKE, 0) == sk.SK_ERR_INVALID_ARG
