@@ -161,6 +161,50 @@ def visible_pairs(w) -> int:
     return total
 
 
+def time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_out, stream, n: int):
+    """Per-step time of counts -> partial -> combine run n times back to back
+    on `stream`: eager launches, then the same three launches captured once
+    as a HIP graph and replayed n times (small workloads are bound by the
+    launches, not the kernels).  The replays must reproduce the eager
+    output bit for bit."""
+    import torch
+
+    from split_kv_attention_amd import _lib
+
+    def run_on(s):
+        _lib.sk_valid_split_counts(prob.c, counts, s)
+        _lib.sk_attn_partial(prob.c, q, k, v, o_part, lse_part, s)
+        _lib.sk_attn_combine(prob.c, o_part, lse_part, counts, out, lse_out, s)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    t_eager = timed(lambda: run_on(stream.cuda_stream))
+    expect = (out.clone(), lse_out.clone())
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run_on(side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    out.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(out, expect[0]) and torch.equal(lse_out, expect[1])):
+        raise RuntimeError("the replayed step differs from the eager one")
+    t_graph = timed(graph.replay)
+    del graph
+    return t_eager, t_graph
+
+
 def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
     """Every workload of the parity suite (or those whose name starts with
     `only`) through counts -> partial -> combine, medians of HIP-event
@@ -208,6 +252,7 @@ def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
         torch.cuda.synchronize()
         t_part = sorted(e[1].elapsed_time(e[2]) for e in evs)[n // 2]
         t_comb = sorted(e[2].elapsed_time(e[3]) for e in evs)[n // 2]
+        t_eager, t_graph = time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_out, stream, n)
 
         H, es = w.heads, q.element_size()
         rows = sum(w.sq)
@@ -231,6 +276,8 @@ def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
                         "frac": achieved / peak, "flop": flop, "algorithmic_bytes": part_bytes},
             "combine": {"ms": t_comb, "gbps": comb_gbps, "frac": comb_gbps / PEAK_HBM_GBPS,
                         "algorithmic_bytes": comb_bytes},
+            "step": {"ms_eager": t_eager, "ms_graph": t_graph,
+                     "tflops_eager": flop / (t_eager * 1e-3) / 1e12, "tflops_graph": flop / (t_graph * 1e-3) / 1e12},
         }
         if oracle_budget_s > 0:
             base = cpu_baseline(w, inputs, prob.m_per_block, budget_s=oracle_budget_s)
@@ -492,6 +539,39 @@ def time_backward(w, prob, inputs, out, lse, stream, steps: int):
     }
 
 
+COLD_COPIES = 8
+
+
+def time_combine_cold_back_to_back(prob, o_part, lse_part, counts, out, lse_out, flush, stream, iters):
+    """Median per-launch time of COLD_COPIES combines launched back to back
+    after a cache flush, each on its own copy of the partials, counts and
+    outputs: every launch reads data no earlier launch touched (the copies
+    together exceed the 256 MB infinity cache), while the dispatch of each
+    overlaps the previous one's execution as in a pipeline."""
+    import torch
+
+    from split_kv_attention_amd import _lib
+
+    sh = stream.cuda_stream
+    copies = [(o_part.clone(), lse_part.clone(), counts.clone(), torch.empty_like(out), torch.empty_like(lse_out))
+              for _ in range(COLD_COPIES)]
+    per_launch = []
+    for _ in range(max(iters, 1)):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for o, l, c, y, ly in copies:
+            _lib.sk_attn_combine(prob.c, o, l, c, y, ly, sh)
+        b.record(stream)
+        per_launch.append((a, b))
+    torch.cuda.synchronize()
+    for _, _, _, y, ly in copies:  # every copy merged the same partials
+        if not (torch.equal(y, out) and torch.equal(ly, lse_out)):
+            raise RuntimeError("a back-to-back combine differs from the pipeline's")
+    del copies
+    return sorted(a.elapsed_time(b) for a, b in per_launch)[len(per_launch) // 2] / COLD_COPIES
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -595,6 +675,8 @@ def main() -> int:
     torch.cuda.synchronize()
     t_combine_cold = sorted(x.elapsed_time(y) for x, y in cold)[len(cold) // 2]
     t_launch_floor = sorted(x.elapsed_time(y) for x, y in floor)[len(floor) // 2]
+    t_combine_cold_b2b = time_combine_cold_back_to_back(prob, o_part, lse_part, counts, out, lse_out, flush, stream,
+                                                        args.cold_iters)
     del flush, tiny
 
     unsplit = time_unsplit(w, inputs, stream, args.steps, t_partial, t_combine, args.warmup)
@@ -662,6 +744,9 @@ def main() -> int:
             "frac_in_pipeline": combine_bytes / (t_combine * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "peak": PEAK_HBM_GBPS,
             "ms_cold_launch_floor": t_launch_floor,
+            "ms_cold_back_to_back": t_combine_cold_b2b,
+            "frac_cold_back_to_back": combine_bytes / (t_combine_cold_b2b * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "cold_back_to_back_launches": COLD_COPIES,
         },
         "counts_ms": t_counts,
         "unsplit": unsplit,
