@@ -172,7 +172,9 @@ int64_t sk_partial_scratch_bytes(const sk_problem* p);
 /* Query rows per M block of the partial kernel selected for `p` (>= 1), or -1
  * if `p` is invalid or unsupported.  The kernel partitions each block's keys
  * with the count formula evaluated at the block's last row (rocmlirTriton
- * page, the paragraph on conservative counts), so the partials depend on it. */
+ * page, the paragraph on conservative counts), so the partials depend on it.
+ * 1 for a 16-bit problem with max_seqlen_q = 1 and head dims 64/64 or
+ * 128/128 (the decode kernel), 64 for f32, 128 otherwise. */
 int32_t sk_partial_m_per_block(const sk_problem* p);
 
 /* Per-row valid-split counts (rocmlirTriton page, "Per-row valid-split

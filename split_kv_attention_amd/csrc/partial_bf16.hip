@@ -546,10 +546,10 @@ int blocks_per_cu() {
 
 template <typename T>
 PartialKernel find_partial_16(int d_qk, int d_v) {
-    if (d_qk == 64 && d_v == 64) return {launch<T, 64, 64>, kBM, blocks_per_cu<T, 64, 64>};
-    if (d_qk == 128 && d_v == 128) return {launch<T, 128, 128>, kBM, blocks_per_cu<T, 128, 128>};
-    if (d_qk == 192 && d_v == 128) return {launch<T, 192, 128>, kBM, blocks_per_cu<T, 192, 128>};
-    return {nullptr, 0, nullptr};
+    if (d_qk == 64 && d_v == 64) return {launch<T, 64, 64>, kBM, blocks_per_cu<T, 64, 64>, true};
+    if (d_qk == 128 && d_v == 128) return {launch<T, 128, 128>, kBM, blocks_per_cu<T, 128, 128>, true};
+    if (d_qk == 192 && d_v == 128) return {launch<T, 192, 128>, kBM, blocks_per_cu<T, 192, 128>, true};
+    return {nullptr, 0, nullptr, false};
 }
 
 PartialKernel find_partial_bf16(int d_qk, int d_v) { return find_partial_16<__bf16>(d_qk, d_v); }

@@ -195,11 +195,11 @@ hipError_t launch(const PartialArgs& a, hipStream_t stream) {
 }  // namespace
 
 PartialKernel find_partial_f32(int d_qk, int d_v) {
-    if (d_qk == 16 && d_v == 16) return {launch<16, 16, 32>, kF32Rows, nullptr};
-    if (d_qk == 32 && d_v == 32) return {launch<32, 32, 32>, kF32Rows, nullptr};
-    if (d_qk == 64 && d_v == 64) return {launch<64, 64, 32>, kF32Rows, nullptr};
-    if (d_qk == 128 && d_v == 128) return {launch<128, 128, 16>, kF32Rows, nullptr};
-    return {nullptr, 0, nullptr};
+    if (d_qk == 16 && d_v == 16) return {launch<16, 16, 32>, kF32Rows, nullptr, false};
+    if (d_qk == 32 && d_v == 32) return {launch<32, 32, 32>, kF32Rows, nullptr, false};
+    if (d_qk == 64 && d_v == 64) return {launch<64, 64, 32>, kF32Rows, nullptr, false};
+    if (d_qk == 128 && d_v == 128) return {launch<128, 128, 16>, kF32Rows, nullptr, false};
+    return {nullptr, 0, nullptr, false};
 }
 
 }  // namespace sk

@@ -349,13 +349,17 @@ typedef hipError_t (*PartialLauncher)(const PartialArgs& a, hipStream_t stream);
 struct PartialKernel {
     PartialLauncher launch;
     int m_per_block;
-    // Workgroups of the kernel resident per CU (for the tail split), or
-    // nullptr when the kernel runs every item whole.
+    // Workgroups of the kernel resident per CU (the automatic split count
+    // and the tail split), or nullptr when unknown.
     int (*blocks_per_cu)();
+    // The kernel can run the last round's items as key pieces (tail split).
+    bool tail_pieces;
 };
-// Kernel for (dtype, d_qk, d_v), or {nullptr, 0} when not built.
+// Kernel for (dtype, d_qk, d_v), or {nullptr, 0, nullptr, false} when not built.
 PartialKernel find_partial_bf16(int d_qk, int d_v);
 PartialKernel find_partial_f16(int d_qk, int d_v);
 PartialKernel find_partial_f32(int d_qk, int d_v);
+// Decode kernel (sequences of at most one query row) for a 16-bit dtype.
+PartialKernel find_partial_decode(int dtype, int d_qk, int d_v);
 
 }  // namespace sk

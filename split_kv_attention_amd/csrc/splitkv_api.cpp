@@ -110,6 +110,12 @@ sk::SeqTable seq_table(const sk_problem& p) {
 bool aligned(const void* ptr, size_t bytes) { return ((uintptr_t)ptr % bytes) == 0; }
 
 sk::PartialKernel pick_partial(const sk_problem& p) {
+    // Decode (every sequence at most one query row): the streaming kernel
+    // where it exists for the head dims.
+    if (p.max_seqlen_q == 1) {
+        const sk::PartialKernel d = sk::find_partial_decode(p.dtype, p.head_dim_qk, p.head_dim_v);
+        if (d.launch) return d;
+    }
     if (p.dtype == SK_BF16) return sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v);
     if (p.dtype == SK_F16) return sk::find_partial_f16(p.head_dim_qk, p.head_dim_v);
     return sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
@@ -138,6 +144,10 @@ int64_t partial_slots(const sk::PartialKernel& k) {
     return (int64_t)k.blocks_per_cu() * cu_count();
 }
 
+// Slots of the tail split: the resident workgroups of a kernel that can run
+// key pieces, else 0 (every item runs whole, no scratch).
+int64_t piece_slots(const sk::PartialKernel& k) { return k.tail_pieces ? partial_slots(k) : 0; }
+
 int64_t piece_scratch_bytes(int64_t items, int64_t m_per_block, int64_t dv) {
     return items * m_per_block * (dv + 1) * (int64_t)sizeof(float);
 }
@@ -154,7 +164,7 @@ TailPlan plan_tail(const sk_problem& p, const sk::PartialKernel& k, int64_t n_wo
                    int64_t scratch_bytes) {
     constexpr int64_t kMinPieceTiles = 8;
     TailPlan none{(uint32_t)n_work, 1};
-    const int64_t slots = partial_slots(k);
+    const int64_t slots = piece_slots(k);
     if (slots <= 0 || !scratch) return none;
     const int64_t tail = n_work % slots;
     if (tail == 0) return none;
@@ -285,7 +295,7 @@ int32_t sk_split_kv(const sk_problem* p) {
 int64_t sk_partial_scratch_bytes(const sk_problem* p) {
     if (check_problem(p) != SK_OK) return -1;
     const sk::PartialKernel k = pick_partial(*p);
-    const int64_t slots = k.launch ? partial_slots(k) : 0;
+    const int64_t slots = k.launch ? piece_slots(k) : 0;
     ok();
     return slots > 0 ? piece_scratch_bytes(slots, k.m_per_block, p->head_dim_v) : 0;
 }
@@ -376,7 +386,7 @@ static sk_status partial_impl(const sk_problem* p, const void* q, const void* k,
     void* scratch = p->partial_scratch;
     int64_t scratch_bytes = p->partial_scratch_bytes;
     if (noalloc) {
-        const int64_t slots = partial_slots(kern);
+        const int64_t slots = piece_slots(kern);
         const int64_t need = slots > 0 ? piece_scratch_bytes(slots, kern.m_per_block, p->head_dim_v) : 0;
         if (need > sk::kStaticScratchBytes)
             return fail(SK_ERR_UNSUPPORTED,

@@ -81,6 +81,29 @@ def test_rows_workspace_and_block_size():
     assert sk.sk_rows(p) == 77
 
 
+def test_one_row_problems_take_the_decode_kernel():
+    """A problem whose sequences hold one query row at most runs on the
+    decode kernel (block of one row, no key pieces) where it exists: 16-bit
+    storage with head dims 64/64 or 128/128."""
+    for dtype in (sk.SK_BF16, sk.SK_F16):
+        for d in (64, 128):
+            p = _good()
+            p.max_seqlen_q, p.dtype, p.out_dtype = 1, dtype, dtype
+            p.head_dim_qk = p.head_dim_v = d
+            assert sk.sk_partial_m_per_block(p) == 1
+            assert _lib.sk_partial_scratch_bytes(p) == 0
+    p = _good()
+    p.max_seqlen_q = 1
+    p.head_dim_qk, p.head_dim_v = 192, 128
+    assert sk.sk_partial_m_per_block(p) == 128  # the MFMA kernel
+    p = _good()
+    p.max_seqlen_q, p.dtype, p.out_dtype = 1, sk.SK_F32, sk.SK_F32
+    assert sk.sk_partial_m_per_block(p) == 64  # the f32 kernel
+    p = _good()
+    p.max_seqlen_q = 2
+    assert sk.sk_partial_m_per_block(p) == 128
+
+
 # A non-NULL, aligned address that is never dereferenced: every call below
 # must fail validation on the host first.
 FAKE = 1 << 20
