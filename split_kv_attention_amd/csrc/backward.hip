@@ -547,7 +547,8 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     const int k1 = (int)min((int64_t)k0 + kKB, sq.lv + 1);
     int q_lo = 0, q_hi = 0;
     if (k1 > k0) {
-        q_lo = mask == SK_MASK_NONE ? 0 : (int)max((int64_t)0, (int64_t)k0 - sq.off);
+        // (clamped to the rows before the cast: the offset is 64-bit)
+        q_lo = mask == SK_MASK_NONE ? 0 : (int)min(max((int64_t)0, (int64_t)k0 - sq.off), (int64_t)sq.sq);
         int64_t hi = sq.sq;
         if (win >= 0) hi = min(hi, (int64_t)k1 - sq.off + win);
         q_hi = (int)max(hi, (int64_t)q_lo);

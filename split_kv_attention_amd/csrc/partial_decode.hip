@@ -95,10 +95,13 @@ __global__ __launch_bounds__(kDecThreads) void partial_decode_kernel(PartialArgs
     if (!in_bounds(a.check, kSiteKeys, (sq.krow0 >= 0 ? sq.krow0 : 0) + ke - 1,
                    sq.krow0 >= 0 ? total_keys(a.seqs, a.batch) : (int64_t)a.seqs.max_sk))
         return;
-    // Keys of the split the row sees: the window's first key, the mask's
-    // last (an empty range leaves O_s = 0, L_s = -inf).
-    const int kb = (int)max((int64_t)ks, vis_first(sq, a.seqs.window_left, 0));
-    const int kend = (int)min((int64_t)ke, vis_last(sq, mask, 0) + 1);
+    // Keys of the split the row sees: from the window's first key to the
+    // mask's last, clamped so that ks <= kb <= kend <= ke whatever the
+    // offset (an empty range leaves O_s = 0, L_s = -inf).
+    const int64_t lo = max((int64_t)ks, vis_first(sq, a.seqs.window_left, 0));
+    const int64_t hi = min((int64_t)ke, vis_last(sq, mask, 0) + 1);
+    const int kb = (int)min(lo, (int64_t)ke);
+    const int kend = (int)max(hi, (int64_t)kb);
 
     const int64_t row = sq.row0;
     const bool row_ok = row < a.rows &&

@@ -120,6 +120,14 @@ BWD = [
     _shrink(workloads.CAUSAL_BF16, name="bwd_unsplit_S1", split_kv=1, sq=(200, 200), sk=(640, 640), mask="none",
             heads=2),
     _shrink(workloads.LONG_PREFILL, name="bwd_auto_split_Sq128_Sk9000", heads=2, sq=(128,), sk=(9000,), split_kv=0),
+    # prefix offsets far outside 32 bits (a 64-bit field): no row sees a key,
+    # every row sees every key, or every window starts past the last key
+    _shrink(workloads.CAUSAL_BF16, name="bwd_offset_far_below", mask="prefix_causal", prefix_offset=-(1 << 40),
+            sq=(130, 130), sk=(200, 200), heads=2),
+    _shrink(workloads.CAUSAL_BF16, name="bwd_offset_far_above", mask="prefix_causal", prefix_offset=1 << 40,
+            sq=(130, 130), sk=(200, 200), heads=2),
+    _shrink(workloads.CAUSAL_BF16, name="bwd_offset_far_above_window", mask="prefix_causal", prefix_offset=1 << 40,
+            window_left=50, sq=(130, 130), sk=(200, 200), heads=2),
 ]
 
 

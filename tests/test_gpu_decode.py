@@ -56,6 +56,14 @@ CASES = [
     _dec("dec_nPB128_ragged", sq=(1,) * 4, sk=(1031,) * 4, heads=2, split_kv=7, n_per_block=128),
     _dec("dec_single_key", sq=(1,) * 4, sk=(1,) * 4, heads=2, split_kv=4),
     _dec("dec_last_valid_short", sq=(1,) * 4, sk=(1000,) * 4, heads=2, split_kv=4, last_valid_kv_index=37),
+    # offsets far outside 32 bits: nothing visible, everything visible, or a
+    # window that starts past the last key
+    _dec("dec_offset_far_below", sq=(1,) * 2, sk=(500,) * 2, heads=2, split_kv=4, mask="prefix_causal",
+         prefix_offset=-(1 << 40)),
+    _dec("dec_offset_far_above", sq=(1,) * 2, sk=(500,) * 2, heads=2, split_kv=4, mask="prefix_causal",
+         prefix_offset=1 << 40),
+    _dec("dec_offset_far_above_window", sq=(1,) * 2, sk=(500,) * 2, heads=2, split_kv=4, mask="prefix_causal",
+         prefix_offset=1 << 40, window_left=10),
 ]
 
 

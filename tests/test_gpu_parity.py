@@ -288,6 +288,28 @@ WINDOW = [
 ]
 
 
+# Prefix offsets far outside 32 bits (the offset is a 64-bit field): no row
+# sees a key, every row sees every key, or every row's window starts past
+# the last key.
+EXTREME_OFFSETS = [
+    _shrink(workloads.LONG_PREFILL, name="offset_far_below", sq=(200,), sk=(700,), mask="prefix_causal",
+            prefix_offset=-(1 << 40)),
+    _shrink(workloads.LONG_PREFILL, name="offset_far_above", sq=(200,), sk=(700,), mask="prefix_causal",
+            prefix_offset=1 << 40),
+    _shrink(workloads.LONG_PREFILL, name="offset_far_above_window", sq=(200,), sk=(700,), mask="prefix_causal",
+            prefix_offset=1 << 40, window_left=50),
+    _shrink(workloads.TINY_F32, name="offset_far_above_f32", mask="prefix_causal", prefix_offset=1 << 40),
+]
+
+
+@pytest.mark.parametrize("w", EXTREME_OFFSETS, ids=lambda w: w.name)
+def test_extreme_prefix_offsets_all_rows(w):
+    log(f"offsets {w.name}")
+    inputs, prob, res = run_gpu(w, seed=14)
+    st = compare(w, inputs, prob, res, label=w.name)
+    log(f"  {st}")
+
+
 @pytest.mark.parametrize("w", WINDOW, ids=lambda w: w.name)
 def test_sliding_window_all_rows(w):
     log(f"window {w.name}")
