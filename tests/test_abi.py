@@ -286,3 +286,113 @@ def test_checked_build_links_and_exports_every_function():
     p = _good()
     p.split_kv = -2
     assert lib.sk_valid_split_counts(ctypes.byref(p), FAKE, 0) == sk.SK_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# Fuzzed problems: every entry point, with NULL tensors, must return a status
+# (nothing can be enqueued without tensors) and the pure host queries must
+# return without crashing, whatever the fields hold.  Under the sanitizer
+# build (test_asan_host.py runs this file) any out-of-bounds host access in
+# argument checking or planning aborts the run.
+# ---------------------------------------------------------------------------
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+_I32 = st.one_of(st.integers(-3, 3), st.sampled_from([0, 1, 8, 63, 64, 65, 127, 128, 129, 192, 255, 256, 257,
+                                                       4096, 65535, 65536, 2**31 - 1, -2**31]),
+                 st.integers(-2**31, 2**31 - 1))
+_I64 = st.one_of(st.integers(-3, 3), st.sampled_from([2**31, -2**31 - 1, 2**40, -2**40, 2**63 - 1, -2**63]),
+                 st.integers(-2**63, 2**63 - 1))
+_PTR = st.sampled_from([None, FAKE])
+_SMALL_DIM = st.sampled_from([-1, 0, 1, 16, 32, 64, 96, 128, 192, 256, 257])
+_FIELDS = st.fixed_dictionaries({
+    "batch": _I32, "num_heads": _I32, "max_seqlen_q": _I32, "max_seqlen_k": _I32, "total_q": _I32,
+    "head_dim_qk": _SMALL_DIM, "head_dim_v": _SMALL_DIM, "split_kv": _I32, "n_per_block": _I32,
+    "mask": st.integers(-1, 3), "dtype": st.integers(-1, 3), "out_dtype": st.integers(-1, 3),
+    "prefix_offset": _I64, "last_valid_kv_index": _I64,
+    "softmax_scale": st.sampled_from([0.0, -1.0, 0.125, 1e-30, 1e30, float("inf"), float("nan")]),
+    "reserved0": st.sampled_from([0, 0, 0, 1]),
+    "cu_seqlens_q": _PTR, "cu_seqlens_k": _PTR, "split_kv_per_seq": _PTR, "prefix_offset_per_seq": _PTR,
+    "last_valid_per_seq": _PTR,
+    "q_stride_row": _I64, "q_stride_head": _I64, "q_stride_batch": _I64,
+    "k_stride_row": _I64, "k_stride_head": _I64, "k_stride_batch": _I64,
+    "v_stride_row": _I64, "v_stride_head": _I64, "v_stride_batch": _I64,
+    "o_stride_row": _I64, "o_stride_head": _I64, "o_stride_batch": _I64,
+    "partial_scratch": _PTR, "partial_scratch_bytes": _I64, "window_left": _I64,
+})
+
+
+@settings(max_examples=400, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(fields=_FIELDS)
+def test_fuzzed_problems_are_answered_on_the_host(fields):
+    p = _lib.SkProblem()
+    for name, value in fields.items():
+        setattr(p, name, value)
+    lib = _lib.load()
+    bp = ctypes.byref(p)
+    # pure host queries
+    lib.sk_rows(bp)
+    lib.sk_split_kv(bp)
+    o, l = ctypes.c_size_t(), ctypes.c_size_t()
+    lib.sk_workspace_bytes(bp, ctypes.byref(o), ctypes.byref(l))
+    lib.sk_partial_scratch_bytes(bp)
+    lib.sk_partial_m_per_block(bp)
+    lib.sk_backward_workspace_bytes(bp)
+    # entry points without tensors: rejected, or a no-op for an empty problem
+    statuses = [
+        lib.sk_valid_split_counts(bp, None, None),
+        lib.sk_attn_partial(bp, None, None, None, None, None, None),
+        lib.sk_attn_partial_noalloc(bp, None, None, None, None, None, None),
+        lib.sk_attn_combine(bp, None, None, None, None, None, None),
+        lib.sk_attn_backward(bp, None, None, None, None, None, None, None, None, None, None, 0, None),
+    ]
+    for s in statuses:
+        assert s in (sk.SK_OK, sk.SK_ERR_INVALID_ARG, sk.SK_ERR_UNSUPPORTED), s
+        if s != sk.SK_OK:
+            assert lib.sk_last_error().decode()
+    if any(s == sk.SK_OK for s in statuses[:4]):
+        # only a problem with no rows may succeed without tensors
+        assert p.batch == 0 or p.max_seqlen_q == 0 or lib.sk_rows(bp) == 0
+
+
+_NEAR = st.fixed_dictionaries({
+    "batch": st.integers(0, 70000), "num_heads": st.integers(1, 70000), "max_seqlen_q": st.integers(0, 300000),
+    "max_seqlen_k": st.integers(0, 2**31 - 1), "head_dim_qk": st.sampled_from([64, 128, 192, 256]),
+    "head_dim_v": st.sampled_from([64, 128]), "split_kv": st.integers(0, 130), "n_per_block": st.integers(1, 4096),
+    "mask": st.integers(0, 2), "dtype": st.integers(0, 2), "prefix_offset": _I64, "last_valid_kv_index": _I64,
+    "window_left": st.one_of(st.just(-1), st.integers(0, 2**40)), "packed": st.booleans(),
+    "total_q": st.integers(0, 2**31 - 1), "per_seq": st.booleans(),
+})
+
+
+@settings(max_examples=400, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(f=_NEAR)
+def test_fuzzed_valid_looking_problems_are_answered_on_the_host(f):
+    """Problems that pass most checks, so that work planning, the automatic
+    split count and the workspace sizes are reached: the same contract."""
+    p = _good()
+    for name in ("batch", "num_heads", "max_seqlen_q", "max_seqlen_k", "head_dim_qk", "head_dim_v", "split_kv",
+                 "n_per_block", "mask", "dtype", "prefix_offset", "last_valid_kv_index", "window_left"):
+        setattr(p, name, f[name])
+    p.out_dtype = f["dtype"]
+    if f["packed"]:
+        p.cu_seqlens_q, p.cu_seqlens_k, p.total_q = FAKE, FAKE, f["total_q"]
+    if f["per_seq"] and f["split_kv"] > 0:
+        p.split_kv_per_seq = p.prefix_offset_per_seq = p.last_valid_per_seq = FAKE
+    lib = _lib.load()
+    bp = ctypes.byref(p)
+    rows = lib.sk_rows(bp)
+    lib.sk_split_kv(bp)
+    lib.sk_workspace_bytes(bp, None, None)
+    lib.sk_partial_scratch_bytes(bp)
+    lib.sk_partial_m_per_block(bp)
+    lib.sk_backward_workspace_bytes(bp)
+    for s in (lib.sk_valid_split_counts(bp, None, None),
+              lib.sk_attn_partial(bp, None, None, None, None, None, None),
+              lib.sk_attn_partial_noalloc(bp, None, None, None, None, None, None),
+              lib.sk_attn_combine(bp, None, None, None, None, None, None)):
+        assert s in (sk.SK_OK, sk.SK_ERR_INVALID_ARG, sk.SK_ERR_UNSUPPORTED), s
+        if s == sk.SK_OK:
+            assert p.batch == 0 or p.max_seqlen_q == 0 or rows == 0
+    s = lib.sk_attn_backward(bp, None, None, None, None, None, None, None, None, None, None, 0, None)
+    assert s in (sk.SK_OK, sk.SK_ERR_INVALID_ARG, sk.SK_ERR_UNSUPPORTED), s
