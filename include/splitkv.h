@@ -279,22 +279,24 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
 int64_t sk_backward_workspace_bytes(const sk_problem* p);
 
 /* Bounds-check report of a checked build of the library (compiled with
- * SK_CHECKED=1: split_kv_attention_amd.build.build_checked).  Its forward
- * kernels (counts, partial, piece merge, combine) test every global index
- * they derive from the problem and the device-side tables against the
- * logical extent it addresses, and skip the access when it falls outside
- * (a Q row reads as zeros; the other sites end the thread's work item).
- * Sites: 1 work item (batch, head, split), 2 Q row (against total_q),
- * 3 last key row of a partial's key range (against cu_seqlens_k[batch], or
- * max_seqlen_k for dense K/V), 4 o_part / lse_part slot, 5 key-piece
- * scratch slot, 6 counts entry, 7 combine row (head, sequence), 8 combine
- * split slot (against split_kv).  Returns the number of failed tests on the
- * current device since the previous call (each thread counts its own) and
- * resets it; the first one's site, index and limit go to the three pointers
- * (each may be NULL).  It synchronises with the device (blocking copies),
- * so call it after the work it reports on has finished.  A normal build
- * returns -1 with SK_ERR_UNSUPPORTED in sk_last_error; -1 with SK_ERR_HIP
- * if the record cannot be read. */
+ * SK_CHECKED=1: split_kv_attention_amd.build.build_checked).  Its kernels
+ * (counts, partial, piece merge, combine and the four backward kernels) test
+ * every global index they derive from the problem and the device-side tables
+ * against the logical extent it addresses, and skip the access when it falls
+ * outside (a Q row reads as zeros; the other sites end the thread's work or
+ * its item).  Sites: 1 work item (batch, head, split), 2 Q row (against
+ * total_q), 3 last key row of a partial's key range (against
+ * cu_seqlens_k[batch], or max_seqlen_k for dense K/V), 4 o_part / lse_part
+ * slot, 5 key-piece scratch slot, 6 counts entry, 7 combine row (head,
+ * sequence), 8 combine split slot (against split_kv), 9 backward work item,
+ * 10 backward query row, 11 backward key row, 12 backward dQ split-sum
+ * slot.  Returns the number of failed tests on the current device since the
+ * previous call (each thread counts its own) and resets it; the first one's
+ * site, index and limit go to the three pointers (each may be NULL).  It
+ * synchronises with the device (blocking copies), so call it after the work
+ * it reports on has finished.  A normal build returns -1 with
+ * SK_ERR_UNSUPPORTED in sk_last_error; -1 with SK_ERR_HIP if the record
+ * cannot be read. */
 int64_t sk_check_violations(int64_t* first_site, int64_t* first_index, int64_t* first_limit);
 
 #ifdef __cplusplus

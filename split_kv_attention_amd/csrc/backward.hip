@@ -213,6 +213,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BackwardArgs a) {
     if (r >= sq.sq) return;
     const int64_t prow = sq.row0 + r;
     if (prow >= a.rows) return;
+    if (!in_bounds(a.check, kSiteBwdRow, a.seqs.cu_q ? prow : (int64_t)b * a.seqs.max_sq + r, a.rows)) return;
     const int64_t o = (a.seqs.cu_q ? prow * a.o_row : (int64_t)b * a.o_batch + (int64_t)r * a.o_row) +
                       (int64_t)h * a.o_head;
     typedef T t8 __attribute__((ext_vector_type(8)));
@@ -255,6 +256,7 @@ void bwd_dq_kernel(BackwardArgs a) {
     w /= a.heads;
     const int split = (int)(w % a.seqs.s_max);
     const int b = (int)(w / a.seqs.s_max);
+    if (!in_bounds(a.check, kSiteBwdItem, b, a.batch) || !in_bounds(a.check, kSiteBwdItem, head, a.heads)) return;
     const Seq sq = load_seq(a.seqs, b);
     if (split >= sq.splits) return;
     const int r0 = tile * kQB;
@@ -263,6 +265,9 @@ void bwd_dq_kernel(BackwardArgs a) {
     int ks, ke;
     block_split_range(sq, mask, a.seqs.n_per_block, min(r0 + kQB, sq.sq) - 1, split, ks, ke);
     if (ks >= ke) return;  // no key for the whole block: not written, not summed
+    if (!in_bounds(a.check, kSiteBwdKey, (sq.krow0 >= 0 ? sq.krow0 : 0) + ke - 1,
+                   sq.krow0 >= 0 ? total_keys(a.seqs, a.batch) : (int64_t)a.seqs.max_sk))
+        return;
     const int64_t win = a.seqs.window_left;
     {
         const int64_t lo_first = vis_first(sq, win, r0);
@@ -273,7 +278,9 @@ void bwd_dq_kernel(BackwardArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int qrow = r0 + wave * 32 + col;
-    const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows;  // (rows: cu_seqlens past total_q)
+    const bool row_ok = qrow < sq.sq && sq.row0 + qrow < a.rows &&
+                        in_bounds(a.check, kSiteBwdRow, a.seqs.cu_q ? sq.row0 + qrow : (int64_t)b * a.seqs.max_sq + qrow,
+                                  a.rows);  // (rows: cu_seqlens past total_q)
     const int64_t prow = sq.row0 + qrow;
     const int vis_q = (int)max(min(vis_last(sq, mask, qrow), (int64_t)0x7fffffff), (int64_t)-1);
     const int lo_q = (int)min(vis_first(sq, win, qrow), (int64_t)0x7fffffff);
@@ -442,6 +449,9 @@ void bwd_dq_kernel(BackwardArgs a) {
     }
 
     if (!row_ok || prow >= a.rows) return;
+    if (!in_bounds(a.check, kSiteBwdPart, ((int64_t)head * a.seqs.s_max + split) * a.rows + prow,
+                   (int64_t)a.heads * a.seqs.s_max * a.rows))
+        return;
     float* op = a.dq_part + (((int64_t)head * a.seqs.s_max + split) * a.rows + prow) * DQK + half * 4;
     const float sc = a.scale;
 #pragma unroll
@@ -464,6 +474,10 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(BackwardArgs a) {
     const int64_t prow = sq.row0 + r;
     if (prow >= a.rows) return;
     const int n = block_populated_splits(sq, a.seqs.mask, a.seqs.n_per_block, kQB, r);
+    if (!in_bounds(a.check, kSiteBwdRow, a.seqs.cu_q ? prow : (int64_t)b * a.seqs.max_sq + r, a.rows) ||
+        (n > 0 && !in_bounds(a.check, kSiteBwdPart, ((int64_t)h * a.seqs.s_max + n - 1) * a.rows + prow,
+                             (int64_t)a.heads * a.seqs.s_max * a.rows)))
+        return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < n; ++s) {
         const float4 x = *reinterpret_cast<const float4*>(
@@ -504,6 +518,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     w /= a.n_ktiles;
     const int head = (int)(w % a.heads);
     const int b = (int)(w / a.heads);
+    if (!in_bounds(a.check, kSiteBwdItem, b, a.batch) || !in_bounds(a.check, kSiteBwdItem, head, a.heads)) return;
     const Seq sq = load_seq(a.seqs, b);
     const int k0 = ktile * kKB;
     if (k0 >= sq.sk) return;
@@ -514,8 +529,9 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int key = k0 + wave * 32 + col;
-    const bool key_ok = key < sq.sk;
     const int64_t krow = sq.krow0 >= 0 ? sq.krow0 + key : key;  // packed key row (dense: index in its batch)
+    const bool key_ok = key < sq.sk && in_bounds(a.check, kSiteBwdKey, krow,
+                                                 sq.krow0 >= 0 ? total_keys(a.seqs, a.batch) : (int64_t)a.seqs.max_sk);
 
     // K^T and V^T fragments (B operands): lane holds X[key][16t + 8 half .. +8]
     v8 kf[DQK / 16], vf[DV / 16];
@@ -553,6 +569,10 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         if (win >= 0) hi = min(hi, (int64_t)k1 - sq.off + win);
         q_hi = (int)max(hi, (int64_t)q_lo);
     }
+    // Every query tile the loop loads lies inside the sequence's rows.
+    if (q_hi > q_lo && !in_bounds(a.check, kSiteBwdRow, (a.seqs.cu_q ? sq.row0 : (int64_t)b * a.seqs.max_sq) + q_hi - 1,
+                                  a.rows))
+        q_hi = q_lo;
     // This lane's key is visible to rows q in [q_first, q_first + q_span]
     // (q_span as unsigned: q is visible iff (unsigned)(q - q_first) <= q_span);
     // a key no row sees gets q_first = 2^31, q_span = 0, which no q < 2^31 meets.

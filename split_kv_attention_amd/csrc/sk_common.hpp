@@ -33,6 +33,10 @@ enum CheckSite : int {
     kSiteCountsRow = 6,    // counts entry written
     kSiteCombineRow = 7,   // row merged by the combine (o_part / lse_part / out / lse_out)
     kSiteCombineSplit = 8, // split slot read by the combine
+    kSiteBwdItem = 9,      // decoded (sequence, head, split) of a backward workgroup
+    kSiteBwdRow = 10,      // query row of the backward (Q, dO, out, LSE, D, dQ)
+    kSiteBwdKey = 11,      // key row of the backward (K, V, dK, dV)
+    kSiteBwdPart = 12,     // dQ split-sum slot of the workspace
 };
 __device__ __forceinline__ bool in_bounds(CheckRecord* rec, int site, int64_t i, int64_t limit) {
 #if SK_CHECKED
@@ -303,6 +307,7 @@ struct BackwardArgs {
     int32_t batch;
     float scale;
     float scale_log2;
+    CheckRecord* check;  // bounds-checked build only (else NULL)
 };
 
 typedef hipError_t (*BackwardLauncher)(const BackwardArgs& a, hipStream_t stream);

@@ -588,6 +588,8 @@ sk_status sk_attn_backward(const sk_problem* p, const void* q, const void* k, co
     a.batch = p->batch;
     a.scale = p->softmax_scale;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    const hipError_t ce = sk::check_record(&a.check);
+    if (ce != hipSuccess) return hip_status(ce, "bounds-check record lookup");
     return hip_status(kern.launch(a, (hipStream_t)stream), "backward kernel launch");
 }
 

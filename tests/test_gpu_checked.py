@@ -1,15 +1,17 @@
 """The bounds-checked build of the library on the GPU, through the C ABI.
 
 libsplitkv_checked.so is the same source compiled with SK_CHECKED=1: each
-forward kernel tests every global index it derives (work item, Q row, key
-range, partial / piece / counts slots, combine row and split) against the
-extent it addresses, skips an access that falls outside and counts it in a
-device record that sk_check_violations reads and resets.
+kernel tests every global index it derives (work item, Q row, key range,
+partial / piece / counts slots, combine row and split, the backward's rows,
+keys and dQ split sums) against the extent it addresses, skips an access
+that falls outside and counts it in a device record that
+sk_check_violations reads and resets.
 
 * Every workload of the parity suite, at full size, and small cases of each
   feature (f16, sliding window, key pieces, causal) run through both builds
   in one process: the checked one reports no violation and writes the same
   bits as the normal one in every buffer.
+* The backward on three cases likewise: no violation, the same gradients.
 * A packed batch whose cu_seqlens_k decreases (sequence 0 claims 8000 keys,
   the table's total is 4000) is reported at the key-range site with the
   table's total as the limit.  K and V hold all 8000 claimed rows, so every
@@ -105,3 +107,44 @@ def test_checked_build_reports_keys_past_the_table_total(checked_lib):
     assert site == SITE_KEYS and limit == total and total <= index < claimed, (site, index, limit)
     # the record was reset by the read
     assert _lib.sk_check_violations(checked_lib)[0] == 0
+
+
+BWD_CASES = [
+    dataclasses.replace(workloads.LONG_PREFILL, name="checked_bwd_prefill_Sq300_Sk2000", sq=(300,), sk=(2000,)),
+    dataclasses.replace(workloads.VARLEN_BATCH_PREFIX, name="checked_bwd_varlen_prefix", sq=(130, 1, 257, 64),
+                        sk=(500, 70, 1500, 3000), heads=2, split_kv_per_seq=(2, 4, 6, 8),
+                        prefix_offset_per_seq=(370, 69, 1243, 2936), last_valid_per_seq=(499, 69, 1499, 2999),
+                        window_left=300),
+    dataclasses.replace(workloads.DECODE_BF16, name="checked_bwd_decode_B4_H4_Sk3000", sq=(1,) * 4,
+                        sk=(3000,) * 4, heads=4),
+]
+
+
+def _backward(lib, prob, inputs, out, lse, dout):
+    q, k, v = inputs["q"], inputs["k"], inputs["v"]
+    grads = [torch.full_like(x, float("nan")) for x in (q, k, v)]
+    nbytes = _lib.sk_backward_workspace_bytes(prob.c)
+    ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    st = lib.sk_attn_backward(ctypes.byref(prob.c), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), *(g.data_ptr() for g in grads), ws.data_ptr(),
+                              nbytes, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.sk_last_error()
+    torch.cuda.synchronize()
+    return grads
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=lambda w: w.name)
+def test_checked_backward_reports_nothing_and_matches(w, checked_lib):
+    log(f"checked backward {w.name}")
+    assert _lib.sk_check_violations(checked_lib)[0] == 0
+    inputs = workloads.make_inputs(w, DEV, seed=8)
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+    fwd = _forward(_lib.load(), prob, inputs)
+    dout = workloads.make_dout(w, DEV, 8)
+    ref = _backward(_lib.load(), prob, inputs, fwd["out"], fwd["lse_out"], dout)
+    got = _backward(checked_lib, prob, inputs, fwd["out"], fwd["lse_out"], dout)
+    n, site, index, limit = _lib.sk_check_violations(checked_lib)
+    assert n == 0, f"{n} violations, first at site {site}: index {index} >= limit {limit}"
+    for name, r, g in zip(("dq", "dk", "dv"), ref, got):
+        assert _same_bits(r, g), name
+        assert not torch.isnan(g).any(), name
