@@ -148,14 +148,17 @@ int64_t sk_rows(const sk_problem* p);
  * `p` is invalid.  It is split_kv, or with split_kv = 0 the automatic choice
  * (aiter page, Technical Details: split only when the keys are long and the
  * query tiles alone do not fill the GPU), re-derived for this device:
- *   items = query tiles of 128 rows x heads (batch x tiles of the longest
- *           sequence, or for a packed batch at most ceil(total_q / 128) + B - 1)
- *   slots = resident workgroups of the bf16 partial kernel (2 per CU)
+ *   items = query blocks x heads, with blocks of the partial kernel chosen
+ *           for `p` (sk_partial_m_per_block: 128 rows, or 1 for the decode
+ *           kernel): batch x blocks of the longest sequence, or for a packed
+ *           batch at most ceil(total_q / block) + B - 1
+ *   slots = resident workgroups of that kernel on the device (2 per CU for
+ *           the 128-row kernel)
  *   S     = clamp(round(slots / items), 2, 8)  if max_seqlen_k >= 8192 and
  *           items <= slots, else 1.
  * The key threshold is the explicit 8192 of that page's contract (its review
  * notes a tile-rounded form that also split 8161..8191 keys).  f32 problems
- * and head dims without a bf16 kernel stay unsplit.  The result depends on
+ * and head dims without a 16-bit kernel stay unsplit.  The result depends on
  * the current device's CU count, so buffers must be sized with the same
  * device current. */
 int32_t sk_split_kv(const sk_problem* p);
