@@ -66,7 +66,7 @@ def test_concurrent_threads_on_their_own_streams():
             stream = torch.cuda.Stream()
             with torch.cuda.stream(stream):
                 bufs = attention.alloc_outputs(prob, inputs["q"], inputs["v"])
-                start.wait()
+                start.wait(timeout=60)
                 for _ in range(ROUNDS):
                     _poison(bufs)
                     attention.run(prob, inputs["q"], inputs["k"], inputs["v"], *bufs, stream=stream)
@@ -81,7 +81,7 @@ def test_concurrent_threads_on_their_own_streams():
             p = _lib.SkProblem()
             ctypes.memmove(ctypes.byref(p), ctypes.byref(setups[0][1].c), ctypes.sizeof(p))
             p.split_kv = -2
-            start.wait()
+            start.wait(timeout=60)
             for _ in range(ROUNDS * 4):
                 st = _lib.load().sk_valid_split_counts(ctypes.byref(p), None, None)
                 assert st == _lib.SK_ERR_INVALID_ARG
@@ -89,8 +89,10 @@ def test_concurrent_threads_on_their_own_streams():
         except BaseException as e:
             errors.append(("failing", e))
 
-    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(CASES))]
-    threads.append(threading.Thread(target=failing))
+    # daemon threads and a barrier timeout: a thread that fails early cannot
+    # leave the others (or the interpreter's exit) waiting
+    threads = [threading.Thread(target=worker, args=(i,), daemon=True) for i in range(len(CASES))]
+    threads.append(threading.Thread(target=failing, daemon=True))
     for t in threads:
         t.start()
     for t in threads:
