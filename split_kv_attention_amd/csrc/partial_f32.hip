@@ -20,19 +20,24 @@ constexpr int kF32Rows = 64;  // query rows per workgroup
 
 // Lanes per query row for head dims DQK, DV: four, or fewer where a lane
 // would not get a whole float4 slice.  (On the tiny 64-dim workload four
-// lanes per row took the kernel from 43 to 23 us, sixteen to 27 us.)
+// lanes per row took the kernel from 43 to 23 us, sixteen to 27 us; DPP row
+// sums instead of LDS shuffles then to 21 us.)
 template <int DQK, int DV>
 constexpr int f32_sub() {
     constexpr int d = DQK < DV ? DQK : DV;
     return d / 4 < 4 ? d / 4 : 4;
 }
 
-// Sum over the SUB consecutive lanes of a row (xor butterfly within each
-// group of SUB lanes).
+// Sum over the SUB consecutive lanes of a row (SUB = 2 or 4: a half quad
+// or a quad), every lane receiving it: DPP quad permutes, which exchange
+// within the row's own lanes without a trip through LDS.
 template <int SUB>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < SUB; m <<= 1) x += __shfl_xor(x, m, SUB);
+    static_assert(SUB == 1 || SUB == 2 || SUB == 4, "a row's lanes sit in one quad");
+    if constexpr (SUB >= 2)  // quad_perm [1, 0, 3, 2]: lane ^ 1
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+    if constexpr (SUB == 4)  // quad_perm [2, 3, 0, 1]: lane ^ 2
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
     return x;
 }
 
