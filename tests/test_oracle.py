@@ -429,6 +429,27 @@ def test_fully_masked_rows_are_exactly_zero():
     assert (O_s[:, :16] == 0).all() and np.isneginf(L_s[:, :16]).all()
 
 
+def test_offsets_beyond_32_bits_reduce_to_the_plain_cases():
+    """A prefix offset of +2^40 makes every key visible (no mask), -2^40 none
+    (every row fully masked, count 1), and +2^40 with a window of w puts
+    every window's start past the last key."""
+    rng = np.random.default_rng(12)
+    sq, sk, d = 9, 40, 6
+    Q, K, V = _rand(rng, sq, d), _rand(rng, sk, d), _rand(rng, sk, 5)
+    plain = oracle.unsplit(Q, K, V, 0.4, SeqSpec(sq, sk, 3, 8, MASK_NONE))
+    far = oracle.unsplit(Q, K, V, 0.4, SeqSpec(sq, sk, 3, 8, MASK_PREFIX_CAUSAL, 1 << 40))
+    np.testing.assert_array_equal(far[0], plain[0])
+    np.testing.assert_array_equal(far[1], plain[1])
+    below = SeqSpec(sq, sk, 3, 8, MASK_PREFIX_CAUSAL, -(1 << 40))
+    O, lse = oracle.unsplit(Q, K, V, 0.4, below)
+    assert (O == 0).all() and np.isneginf(lse).all()
+    assert (oracle.valid_split_counts(below) == 1).all()
+    win = SeqSpec(sq, sk, 3, 8, MASK_PREFIX_CAUSAL, 1 << 40, window_left=5)
+    O, lse = oracle.unsplit(Q, K, V, 0.4, win)
+    assert (O == 0).all() and np.isneginf(lse).all()
+    assert (oracle.valid_split_counts(win) == oracle.valid_split_counts(SeqSpec(sq, sk, 3, 8, MASK_NONE))).all()
+
+
 def test_empty_key_sequence():
     """Empty K returns zero output and -inf LSE instead of an error (aiter review)."""
     Q = np.ones((3, 4))
