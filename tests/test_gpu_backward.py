@@ -284,3 +284,39 @@ def test_backward_rejects_f32_and_mismatched_out_dtype():
     q = inputs["q"]
     with pytest.raises(_lib.SplitKVError, match="SK_ERR_UNSUPPORTED"):
         _lib.sk_attn_backward(prob.c, q, q, q, q, q, q, q, q, q, q, 1 << 20)
+
+
+def _draw_backward(seed: int):
+    """A seeded random backward case: storage type, head dims, dense or
+    packed (sequences may have no row or no key), mask, per-sequence offsets,
+    last valid keys and a window."""
+    rng = np.random.default_rng(8100 + seed)
+    dtype = str(rng.choice(["bf16", "f16"]))
+    d_qk, d_v = [(64, 64), (128, 128), (192, 128)][rng.integers(3)]
+    B = int(rng.integers(1, 4))
+    packed = bool(rng.random() < 0.6)
+    if packed:
+        sq = [int(x) for x in rng.integers(0, 201, B)]
+        sk = [int(x) for x in rng.integers(0, 1501, B)]
+        if max(sq) == 0:
+            sq[0] = 1
+    else:
+        sq, sk = [int(rng.integers(1, 201))] * B, [int(rng.integers(1, 1501))] * B
+    mask = str(rng.choice(["none", "causal", "prefix_causal"]))
+    offsets = tuple(int(sk[b] - sq[b] + rng.integers(-40, 41)) for b in range(B)) if mask == "prefix_causal" else None
+    last_valid = tuple(int(rng.integers(-1, max(sk[b], 1))) for b in range(B)) if rng.random() < 0.3 else None
+    window = int(rng.integers(0, 400)) if rng.random() < 0.3 else -1
+    return workloads.Workload(f"bwd_rand{seed}_{dtype}_D{d_qk}x{d_v}_{'packed' if packed else 'dense'}_{mask}",
+                              heads=int(rng.integers(1, 4)), sq=tuple(sq), sk=tuple(sk), d_qk=d_qk, d_v=d_v,
+                              split_kv=int(rng.integers(1, 9)), n_per_block=int(rng.choice([16, 64, 128])),
+                              mask=mask, packed=packed, dtype=dtype, prefix_offset_per_seq=offsets,
+                              last_valid_per_seq=last_valid, window_left=window)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_backward_random_configurations(seed):
+    w = _draw_backward(seed)
+    log(f"backward random {w.name} sq={w.sq} sk={w.sk} off={w.prefix_offset_per_seq} lv={w.last_valid_per_seq} "
+        f"win={w.window_left}")
+    inputs, dout, dq, dk, dv = run_backward(w, seed=seed)
+    log(f"  {compare_all(w, inputs, dout, dq, dk, dv)}")

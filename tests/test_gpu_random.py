@@ -6,7 +6,8 @@ head-dimension pair the kernels take for it; a dense batch or a packed one
 of 1-4 sequences with 0-300 query rows and 0-2500 keys each; 1-4 heads;
 split_kv 1-12, sometimes per sequence; the key tile n_per_block; the mask
 (none, causal, prefix-causal with per-sequence offsets that may be
-negative); sometimes a last valid key per sequence and a sliding window.
+negative); sometimes a last valid key per sequence and a sliding window;
+and the output type (mostly the input's, else f32 or the other 16-bit one).
 The oracle follows the pages' steps for whatever the draw gives, so the
 draws reach combinations no hand-written case names: ragged row blocks
 against small key tiles, empty sequences beside long ones, per-sequence
@@ -14,6 +15,7 @@ split counts above a sequence's key count, windows narrower than a tile.
 """
 import numpy as np
 import pytest
+import torch
 
 from parity import compare, log, run_gpu
 from split_kv_attention_amd.workloads import Workload
@@ -59,11 +61,26 @@ def draw(seed: int) -> Workload:
                     window_left=window)
 
 
+def draw_out_dtype(seed: int, w: Workload):
+    """The output type, from a generator of its own (so the draws above stay
+    as they are): mostly the input type, else f32 or the other 16-bit type."""
+    rng = np.random.default_rng(57000 + seed)
+    pick = rng.random()
+    if pick < 0.6:
+        return None
+    if pick < 0.8 or w.dtype == "f32":
+        return torch.float32
+    return torch.float16 if w.dtype == "bf16" else torch.bfloat16
+
+
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration_all_rows(seed):
     w = draw(seed)
+    out_dtype = draw_out_dtype(seed, w)
     log(f"random {w.name} sq={w.sq} sk={w.sk} splits={w.split_kv_per_seq} off={w.prefix_offset_per_seq} "
-        f"lv={w.last_valid_per_seq}")
-    inputs, prob, res = run_gpu(w, seed=seed)
+        f"lv={w.last_valid_per_seq} out={out_dtype}")
+    inputs, prob, res = run_gpu(w, seed=seed, out_dtype=out_dtype)
+    if out_dtype is not None:
+        assert res["out"].dtype == out_dtype
     st = compare(w, inputs, prob, res, label=w.name)
     log(f"  {st}")
