@@ -165,8 +165,9 @@ def time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_
     """Per-step time of counts -> partial -> combine run n times back to back
     on `stream`: eager launches, then the same three launches captured once
     as a HIP graph and replayed n times (small workloads are bound by the
-    launches, not the kernels).  The replays must reproduce the eager
-    output bit for bit."""
+    launches, not the kernels), and eagerly with two launches, the combine
+    computing each row's count itself (no counts array).  The replays and
+    the two-launch steps must reproduce the eager output bit for bit."""
     import torch
 
     from split_kv_attention_amd import _lib
@@ -202,7 +203,16 @@ def time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_
         raise RuntimeError("the replayed step differs from the eager one")
     t_graph = timed(graph.replay)
     del graph
-    return t_eager, t_graph
+
+    def two_launches():
+        _lib.sk_attn_partial(prob.c, q, k, v, o_part, lse_part, stream.cuda_stream)
+        _lib.sk_attn_combine(prob.c, o_part, lse_part, None, out, lse_out, stream.cuda_stream)
+
+    out.fill_(float("nan"))
+    t_inline = timed(two_launches)
+    if not (torch.equal(out, expect[0]) and torch.equal(lse_out, expect[1])):
+        raise RuntimeError("the step with inline counts differs from the eager one")
+    return t_eager, t_graph, t_inline
 
 
 def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
@@ -252,7 +262,8 @@ def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
         torch.cuda.synchronize()
         t_part = sorted(e[1].elapsed_time(e[2]) for e in evs)[n // 2]
         t_comb = sorted(e[2].elapsed_time(e[3]) for e in evs)[n // 2]
-        t_eager, t_graph = time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_out, stream, n)
+        t_eager, t_graph, t_inline = time_step_eager_and_graph(prob, q, k, v, counts, o_part, lse_part, out, lse_out,
+                                                               stream, n)
 
         H, es = w.heads, q.element_size()
         rows = sum(w.sq)
@@ -276,7 +287,7 @@ def sweep(only: str | None = None, oracle_budget_s: float = 0.0) -> None:
                         "frac": achieved / peak, "flop": flop, "algorithmic_bytes": part_bytes},
             "combine": {"ms": t_comb, "gbps": comb_gbps, "frac": comb_gbps / PEAK_HBM_GBPS,
                         "algorithmic_bytes": comb_bytes},
-            "step": {"ms_eager": t_eager, "ms_graph": t_graph,
+            "step": {"ms_eager": t_eager, "ms_graph": t_graph, "ms_inline_counts": t_inline,
                      "tflops_eager": flop / (t_eager * 1e-3) / 1e12, "tflops_graph": flop / (t_graph * 1e-3) / 1e12},
         }
         if oracle_budget_s > 0:
