@@ -2,8 +2,9 @@
 
 Small cases are compared on every row; the full-size workloads, in the launch
 configuration the benchmark times, on every row and head (long-context
-prefill, prefix-causal packed batch) or on sampled rows / (sequence, head)
-pairs.
+prefill, both packed batches), on every (sequence, head) pair (decode, the
+oracle fed one sequence at a time), or on sampled rows (the long-context
+prefill with f16 storage).
 """
 import dataclasses
 import json
