@@ -2,9 +2,8 @@
 
 Small cases are compared on every row; the full-size workloads, in the launch
 configuration the benchmark times, on every row and head (long-context
-prefill, both packed batches), on every (sequence, head) pair (decode, the
-oracle fed one sequence at a time), or on sampled rows (the long-context
-prefill with f16 storage).
+prefill in bf16 and f16 storage, both packed batches) or on every
+(sequence, head) pair (decode, the oracle fed one sequence at a time).
 """
 import dataclasses
 import json
@@ -461,32 +460,22 @@ def test_full_decode_every_head():
     torch.cuda.empty_cache()
 
 
-def test_full_prefill_f16_sampled_rows():
-    """f16 storage at the long-context prefill's full size (H = 12, Sq = 4096,
-    Sk = 42700, split 3) in the benchmark's launch configuration: sampled
-    rows (tile edges and random) of three heads against the oracle."""
-    w = _shrink(workloads.LONG_PREFILL, name="varlen_prefill_f16_H12_Sq4096_Sk42700_D192x128_S3", dtype="f16")
-    log(f"full {w.name}")
-    inputs, prob, res = run_gpu(w)
-    assert res["out"].dtype == torch.float16
-    rows_per_seq = {0: sample_rows(w.sq[0], 12, seed=5, tile=prob.m_per_block)}
-    st = compare(w, inputs, prob, res, rows_per_seq=rows_per_seq, heads=[0, 6, 11], label=w.name)
-    log(f"  {st}")
-    assert torch.isfinite(res["out"]).all()
-    del inputs, res
-    torch.cuda.empty_cache()
+LONG_PREFILL_F16 = _shrink(workloads.LONG_PREFILL, name="varlen_prefill_f16_H12_Sq4096_Sk42700_D192x128_S3",
+                           dtype="f16")
 
 
-@pytest.mark.parametrize("w", [workloads.LONG_PREFILL, workloads.VARLEN_BATCH, workloads.VARLEN_BATCH_PREFIX],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [workloads.LONG_PREFILL, LONG_PREFILL_F16, workloads.VARLEN_BATCH,
+                               workloads.VARLEN_BATCH_PREFIX], ids=lambda w: w.name)
 def test_full_prefill_every_row_and_head(w):
-    """The long-context prefill (H = 12, Sq = 4096, Sk = 42700, split 3) and
-    the packed batch (4 x Sq = 4096, Sk 8K..128K, splits 2..8), without mask
-    and prefix-causal, at full size on every row of every head: counts,
-    partials and the merged output and LSE against the oracle (about 1 s of
-    host time per head for the prefill, five times that for the batches)."""
+    """The long-context prefill (H = 12, Sq = 4096, Sk = 42700, split 3), in
+    bf16 and in f16 storage, and the packed batch (4 x Sq = 4096, Sk
+    8K..128K, splits 2..8), without mask and prefix-causal, at full size on
+    every row of every head: counts, partials and the merged output and LSE
+    against the oracle (about 1 s of host time per head for the prefill,
+    five times that for the batches)."""
     log(f"full {w.name}, every row and head")
     inputs, prob, res = run_gpu(w)
+    assert res["out"].dtype == w.torch_dtype
     host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inputs.items()}
     stats = []
     for h in range(w.heads):
