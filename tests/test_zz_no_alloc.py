@@ -79,3 +79,19 @@ def test_noalloc_ignores_the_callers_scratch_and_rejects_bad_arguments():
         _lib.sk_attn_partial_noalloc(prob.c, None, inputs["k"], inputs["v"], got["o_part"], got["lse_part"])
     torch.cuda.synchronize()
     assert np.isfinite(got["out"].float().cpu().numpy()).all()
+
+
+def test_noalloc_on_the_decode_kernel_needs_no_scratch():
+    """One-row sequences run on the decode kernel, which uses no piece
+    scratch: the no-alloc call gives the same bits and needs none."""
+    w = dataclasses.replace(workloads.DECODE_BF16, name="noalloc_decode_B8_H4_Sk3000", sq=(1,) * 8, sk=(3000,) * 8,
+                            heads=4)
+    inputs = workloads.make_inputs(w, DEV, seed=13)
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+    assert prob.m_per_block == 1 and _lib.sk_partial_scratch_bytes(prob.c) == 0
+    ref = _partials(prob, inputs, _lib.sk_attn_partial, scratch=True)
+    got = _partials(prob, inputs, _lib.sk_attn_partial_noalloc, scratch=True)
+    assert _same(got["o_part"], ref["o_part"]) and _same(got["lse_part"], ref["lse_part"])
+    assert torch.equal(got["out"], ref["out"]) and torch.equal(got["lse_out"], ref["lse_out"])
+    st = compare(w, inputs, prob, got, label=f"{w.name} noalloc")
+    log(f"  {st}")
