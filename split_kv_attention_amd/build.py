@@ -6,6 +6,8 @@ Usage:  python -m split_kv_attention_amd.build   (or __graft_entry__.build()).
 
 build_checked() makes libsplitkv_checked.so, whose forward kernels guard every
 global index (compile flag SK_CHECKED, reported by sk_check_violations).
+build_c_client() compiles tests/c_client/sk_client.c, a plain C99 client of
+the ABI, with gcc against the built library.
 build_asan() makes a copy of the library whose HOST code is built with
 AddressSanitizer (device code unchanged) in _build/asan/; a process that loads
 it must preload the sanitizer runtime (asan_runtime()).  It exists for the
@@ -123,6 +125,30 @@ def build_checked() -> str:
     split_kv_attention_amd/libsplitkv_checked.so beside the normal library;
     returns its path."""
     return _build_lib(CHECKED_LIB_PATH, ["-DSK_CHECKED=1"], os.path.join(BUILD, "checked"))
+
+
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "sk_client.c")
+C_CLIENT_PATH = os.path.join(ROOT, "tests", "c_client", "sk_client")
+
+
+def rocm_root() -> str:
+    return os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+
+
+def build_c_client() -> str:
+    """Compile the plain C99 client of the ABI (tests/c_client/sk_client.c)
+    with gcc against the in-tree libsplitkv.so and the HIP runtime; returns
+    its path.  It finds the library beside the package at run time."""
+    rocm = rocm_root()
+    tmp = C_CLIENT_PATH + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+           f"-I{rocm}/include", C_CLIENT_SRC, f"-L{PKG}", "-lsplitkv", f"-L{rocm}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../split_kv_attention_amd", f"-Wl,-rpath,{rocm}/lib", "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, C_CLIENT_PATH)
+    return C_CLIENT_PATH
 
 
 if __name__ == "__main__":

@@ -396,3 +396,13 @@ def test_fuzzed_valid_looking_problems_are_answered_on_the_host(f):
             assert p.batch == 0 or p.max_seqlen_q == 0 or rows == 0
     s = lib.sk_attn_backward(bp, None, None, None, None, None, None, None, None, None, None, 0, None)
     assert s in (sk.SK_OK, sk.SK_ERR_INVALID_ARG, sk.SK_ERR_UNSUPPORTED), s
+
+
+def test_plain_c_client_compiles_against_the_header():
+    """tests/c_client/sk_client.c (a C99 program that includes only the
+    header and the HIP runtime API) builds with -Wall -Wextra -Werror and
+    links libsplitkv.so by name."""
+    exe = build.build_c_client()
+    assert os.access(exe, os.X_OK)
+    deps = subprocess.run(["ldd", exe], capture_output=True, text=True).stdout
+    assert "libsplitkv.so" in deps
