@@ -149,11 +149,12 @@ int64_t sk_rows(const sk_problem* p);
  * (aiter page, Technical Details: split only when the keys are long and the
  * query tiles alone do not fill the GPU), re-derived for this device:
  *   items = query blocks x heads, with blocks of the partial kernel chosen
- *           for `p` (sk_partial_m_per_block: 128 rows, or 1 for the decode
- *           kernel): batch x blocks of the longest sequence, or for a packed
- *           batch at most ceil(total_q / block) + B - 1
+ *           for `p` with split_kv = 1 (sk_partial_m_per_block: 128 or 256
+ *           rows, or 1 for the decode kernel): batch x blocks of the longest
+ *           sequence, or for a packed batch at most ceil(total_q / block) +
+ *           B - 1
  *   slots = resident workgroups of that kernel on the device (2 per CU for
- *           the 128-row kernel)
+ *           the 128-row kernel, 1 for the 256-row one)
  *   S     = clamp(round(slots / items), 2, 8)  if max_seqlen_k >= 8192 and
  *           items <= slots, else 1.
  * The key threshold is the explicit 8192 of that page's contract (its review
@@ -177,7 +178,12 @@ int64_t sk_partial_scratch_bytes(const sk_problem* p);
  * with the count formula evaluated at the block's last row (rocmlirTriton
  * page, the paragraph on conservative counts), so the partials depend on it.
  * 1 for a 16-bit problem with max_seqlen_q = 1 and head dims 64/64 or
- * 128/128 (the decode kernel), 64 for f32, 128 otherwise. */
+ * 128/128 (the decode kernel), 64 for f32.  Other 16-bit problems: 256 when
+ * the partial grid at 256-row blocks, ceil(max_seqlen_q / 256) x num_heads x
+ * split_kv (resolved) x batch items, has at least one item per CU of the
+ * current device, else 128 (and 128 when no device is present).  Like the
+ * automatic split count, the value depends on the current device, so every
+ * call for one problem must see the same device current. */
 int32_t sk_partial_m_per_block(const sk_problem* p);
 
 /* Per-row valid-split counts (rocmlirTriton page, "Per-row valid-split

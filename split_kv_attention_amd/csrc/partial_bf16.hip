@@ -10,7 +10,8 @@
 // "[ASM][HIP][JIT][gfx942] Optimize long-context FMHA with split-KV"
 // (D_qk = 192, D_v = 128), re-designed for gfx950:
 //
-//  * 4 waves, 32 query rows each.  GEMM0 is computed transposed, S^T = K Q^T,
+//  * 32 query rows per wave, in groups of 4 waves (one per SIMD).  GEMM0 is
+//    computed transposed, S^T = K Q^T,
 //    with v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and Q^T
 //    (kept in registers for the whole key loop) the B operand.  The
 //    accumulator then gives every lane ONE query column and 16 keys, so the
@@ -25,6 +26,12 @@
 //    register staging), double-buffered: the next tile streams in while the
 //    current one is multiplied, with one barrier per tile.  16-byte chunks are
 //    XOR-swizzled by row so both operand reads are bank-conflict free.
+//  * Large problems take two groups (8 waves, 256 rows, one workgroup per
+//    CU): every tile is loaded once for twice the rows.  The second group
+//    passes the tile's barrier between its GEMM0 and GEMM1, the first after
+//    its GEMM1, so the two waves that share a SIMD (waves w and w + 4) run
+//    opposite halves of the tile step: one's softmax beside the other's
+//    MFMAs.  V then takes three LDS slots (one group still reads tile t - 1).
 //  * Online softmax in base 2 with the scale folded into one FMA per score;
 //    the reference max moves only when it grows by more than 2^8, and a row
 //    with no visible key so far keeps m = -inf and zero weights.
@@ -45,20 +52,24 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kBM = 128;    // query rows per workgroup
-constexpr int kBN = 64;     // keys per tile
-constexpr int kThreads = 256;
+constexpr int kGroupRows = 128;    // query rows per group of 4 waves
+constexpr int kGroupThreads = 256;
+constexpr int kBN = 64;            // keys per tile
 
-template <int DQK, int DV>
+template <int DQK, int DV, int G>
 struct Cfg {
+    static constexpr int kBM = G * kGroupRows;           // query rows per workgroup
+    static constexpr int kThreads = G * kGroupThreads;
+    static constexpr int V_SLOTS = G == 1 ? 2 : 3;       // LDS slots of V tiles
     static constexpr int KCH = DQK / 8;                 // 16-byte chunks per K row
     static constexpr int VCH = DV / 8;                  // 16-byte chunks per V row
     static constexpr int K_ELEMS = kBN * DQK;           // one K tile (bf16 elements)
     static constexpr int V_ELEMS = kBN * DV;            // one V tile
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int LDS_ELEMS = 2 * K_ELEMS + V_SLOTS * V_ELEMS;
     static constexpr int K_LOADS = kBN * KCH / kThreads;  // 16-byte loads per thread per tile
     static constexpr int V_LOADS = kBN * VCH / kThreads;
     static constexpr int VG = (VCH / 4) < 4 ? (VCH / 4) : 4;  // V swizzle period (rows)
+    static_assert(G == 1 || G == 2, "one or two groups of 4 waves");
     static_assert(DQK % 64 == 0 && DV % 32 == 0, "head dims must be multiples of 64 (QK) and 32 (V)");
     static_assert((kBN * KCH) % kThreads == 0 && (kBN * VCH) % kThreads == 0, "whole loads per thread");
     static_assert(K_LOADS + V_LOADS <= DQK / 16, "one tile load per GEMM0 step");
@@ -70,14 +81,16 @@ struct Cfg {
 // and LSE = m' + log(sum p) are unchanged; weights stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <typename T, int DQK, int DV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <typename T, int DQK, int DV, int G>
+__global__ __launch_bounds__(G * kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void partial_bf16_kernel(PartialArgs a) {
-    using C = Cfg<DQK, DV>;
+    using C = Cfg<DQK, DV, G>;
+    constexpr int kBM = C::kBM;
+    constexpr int kThreads = C::kThreads;
     using E = Elem<T>;
     using bf16x8 = typename E::v8;  // operand vector of the storage type
     using bf16x2 = typename E::v2;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
 
     // Workgroups past n_main run piece `piece` of tail item n_main + tail_i.
     uint32_t item = blockIdx.x;
@@ -129,6 +142,7 @@ void partial_bf16_kernel(PartialArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases in SGPRs
+    const bool late = G > 1 && wave >= 4;  // second group: barrier between GEMM0 and GEMM1
     const int lane = tid & 63;
     const int col = lane & 31;   // query column of this lane (and A-row for loads)
     const int half = lane >> 5;  // which 8-wide k slice / which 4 accumulator rows
@@ -189,9 +203,12 @@ void partial_bf16_kernel(PartialArgs a) {
         const int r = P / C::VCH;
         v_off[i] = (uint32_t)(r * a.v_row + v_swz<C::VG>(r, P % C::VCH) * 8) * 2u;
     }
-    // LDS: K tiles in two slots, V tiles in two slots.  K runs one tile ahead
-    // of V: between tile t's softmax and its GEMM1, GEMM0 of tile t + 1
-    // reads the other K slot.
+    // LDS: K tiles in two slots, V tiles in two (one group) or three slots.
+    // K runs one tile ahead of V: between tile t's softmax and its GEMM1,
+    // GEMM0 of tile t + 1 reads the other K slot.  With two groups, the
+    // second group's GEMM1 of tile t runs after the barrier that ends the
+    // tile, beside the first group's GEMM1 of tile t + 1 and the DMA of
+    // V(t + 2): three V slots.
     uint16_t* const Ks0 = smem;
     uint16_t* const Vs0 = smem + 2 * C::K_ELEMS;
     // The buffer range of a tile ends with the split's last key, so rows past
@@ -442,8 +459,14 @@ void partial_bf16_kernel(PartialArgs a) {
 
     // Pipeline.  Iteration i: the weights of tile i from its scores; GEMM0(i+1)
     // from K slot (i+1)%2 into the same score registers, with the DMA of
-    // K(i+2) -> K slot i%2 and V(i+1) -> V slot (i+1)%2 spread over its steps;
-    // GEMM1(i) from V slot i%2; then tile i+1's mask / max update.
+    // K(i+2) -> K slot i%2 and V(i+1) -> the V slot after tile i's spread
+    // over its steps; GEMM1(i); then tile i+1's mask / max update.  Every
+    // wave passes one barrier per iteration: the first group after GEMM1(i),
+    // the second before it.  The loads a barrier covers were issued before it
+    // by every wave (in GEMM0), and a slot is refilled only after the
+    // barrier that follows its last reader: K(i) is last read by GEMM0(i)
+    // in iteration i - 1; V(i - 2) by the second group's GEMM1(i - 2), which
+    // runs between the barriers of iterations i - 2 and i - 1.
     const int ntiles = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
     if (ntiles > 0) {
         issue_k(ks, 0);
@@ -457,6 +480,7 @@ void partial_bf16_kernel(PartialArgs a) {
             sc_max = prepare(ks, sc);
         }
         sync_tiles();
+        int vs_cur = 0, vs_next = 1;  // V slots of tiles i and i + 1
         for (int i = 0; i + 1 < ntiles; ++i) {
             const int kt = ks + i * kBN;
             // K(i + 2) and V(i + 1), one load per GEMM0 step: issued as one
@@ -470,23 +494,27 @@ void partial_bf16_kernel(PartialArgs a) {
                 weights(sc, pf, rs);
                 check_weights(sc_max, sc, pf, rs);
                 gemm0(Ks0 + ((i + 1) & 1) * C::K_ELEMS, sc, [&](auto step_c) {
-                    issue_one(rk, rv, i & 1, (i + 1) & 1, step_c);
+                    issue_one(rk, rv, i & 1, vs_next, step_c);
                 });
-                gemm1(Vs0 + (i & 1) * C::V_ELEMS, pf);
+                if (late) sync_tiles();
+                gemm1(Vs0 + vs_cur * C::V_ELEMS, pf);
                 sc_max = prepare(kt + kBN, sc);
+                if (!late) sync_tiles();
             } else {
                 [&]<int... L>(std::integer_sequence<int, L...>) {
-                    (issue_one(rk, rv, i & 1, (i + 1) & 1, std::integral_constant<int, L>{}), ...);
+                    (issue_one(rk, rv, i & 1, vs_next, std::integral_constant<int, L>{}), ...);
                 }(std::make_integer_sequence<int, C::K_LOADS + C::V_LOADS>{});
+                sync_tiles();
             }
-            sync_tiles();
+            vs_cur = vs_next;
+            vs_next = vs_next + 1 == C::V_SLOTS ? 0 : vs_next + 1;
         }
         if (wave_active) {
             bf16x8 pf[2][2];
             float rs;
             weights(sc, pf, rs);
             check_weights(sc_max, sc, pf, rs);
-            gemm1(Vs0 + ((ntiles - 1) & 1) * C::V_ELEMS, pf);
+            gemm1(Vs0 + vs_cur * C::V_ELEMS, pf);
         }
     }
 
@@ -519,40 +547,46 @@ void partial_bf16_kernel(PartialArgs a) {
     if (half == 0) *lp = empty ? -INFINITY : m_i * a.scale + logf(l_tot);
 }
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, int G>
 hipError_t launch(const PartialArgs& a, hipStream_t stream) {
     const uint32_t n_tail = a.n_work - a.n_main;
     const uint32_t grid = a.n_main + n_tail * (uint32_t)a.pieces;
-    hipLaunchKernelGGL((partial_bf16_kernel<T, DQK, DV>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_bf16_kernel<T, DQK, DV, G>), dim3(grid), dim3(G * kGroupThreads), 0, stream, a);
     if (n_tail > 0) {
-        launch_merge_pieces<kBM, DV>(a, n_tail, stream);
+        launch_merge_pieces<G * kGroupRows, DV>(a, n_tail, stream);
     }
     return hipGetLastError();
 }
 
 // Resident workgroups per CU (the same on every gfx950 device; cached).
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, int G>
 int blocks_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n > 0) return n;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<T, DQK, DV>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_bf16_kernel<T, DQK, DV, G>, G * kGroupThreads, 0) !=
+        hipSuccess)
         return 0;
     cached.store(n, std::memory_order_relaxed);
     return n;
 }
 
-}  // namespace
-
-template <typename T>
+template <typename T, int G>
 PartialKernel find_partial_16(int d_qk, int d_v) {
-    if (d_qk == 64 && d_v == 64) return {launch<T, 64, 64>, kBM, blocks_per_cu<T, 64, 64>, true};
-    if (d_qk == 128 && d_v == 128) return {launch<T, 128, 128>, kBM, blocks_per_cu<T, 128, 128>, true};
-    if (d_qk == 192 && d_v == 128) return {launch<T, 192, 128>, kBM, blocks_per_cu<T, 192, 128>, true};
+    constexpr int bm = G * kGroupRows;
+    if (d_qk == 64 && d_v == 64) return {launch<T, 64, 64, G>, bm, blocks_per_cu<T, 64, 64, G>, true};
+    if (d_qk == 128 && d_v == 128) return {launch<T, 128, 128, G>, bm, blocks_per_cu<T, 128, 128, G>, true};
+    if (d_qk == 192 && d_v == 128) return {launch<T, 192, 128, G>, bm, blocks_per_cu<T, 192, 128, G>, true};
     return {nullptr, 0, nullptr, false};
 }
 
-PartialKernel find_partial_bf16(int d_qk, int d_v) { return find_partial_16<__bf16>(d_qk, d_v); }
-PartialKernel find_partial_f16(int d_qk, int d_v) { return find_partial_16<_Float16>(d_qk, d_v); }
+}  // namespace
+
+PartialKernel find_partial_bf16(int d_qk, int d_v, bool two_groups) {
+    return two_groups ? find_partial_16<__bf16, 2>(d_qk, d_v) : find_partial_16<__bf16, 1>(d_qk, d_v);
+}
+PartialKernel find_partial_f16(int d_qk, int d_v, bool two_groups) {
+    return two_groups ? find_partial_16<_Float16, 2>(d_qk, d_v) : find_partial_16<_Float16, 1>(d_qk, d_v);
+}
 
 }  // namespace sk

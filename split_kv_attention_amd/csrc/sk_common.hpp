@@ -361,8 +361,10 @@ struct PartialKernel {
     bool tail_pieces;
 };
 // Kernel for (dtype, d_qk, d_v), or {nullptr, 0, nullptr, false} when not built.
-PartialKernel find_partial_bf16(int d_qk, int d_v);
-PartialKernel find_partial_f16(int d_qk, int d_v);
+// The 16-bit MFMA kernels come with one group of 4 waves (128 query rows per
+// workgroup) or two (256 rows, one workgroup per CU).
+PartialKernel find_partial_bf16(int d_qk, int d_v, bool two_groups);
+PartialKernel find_partial_f16(int d_qk, int d_v, bool two_groups);
 PartialKernel find_partial_f32(int d_qk, int d_v);
 // Decode kernel (sequences of at most one query row) for a 16-bit dtype.
 PartialKernel find_partial_decode(int dtype, int d_qk, int d_v);

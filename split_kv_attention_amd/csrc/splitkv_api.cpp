@@ -109,15 +109,38 @@ sk::SeqTable seq_table(const sk_problem& p) {
 
 bool aligned(const void* ptr, size_t bytes) { return ((uintptr_t)ptr % bytes) == 0; }
 
-sk::PartialKernel pick_partial(const sk_problem& p) {
+int cu_count();
+int32_t auto_split_kv(const sk_problem& p);
+
+// Work items (query blocks x heads x splits x sequences) of the partial
+// grid at query blocks of m_per_block rows.
+int64_t partial_work_items(const sk_problem& p, int64_t m_per_block) {
+    return (p.max_seqlen_q + m_per_block - 1) / m_per_block * p.num_heads * p.split_kv * (int64_t)p.batch;
+}
+
+// The partial kernel of a problem: a function of the problem (its split
+// count resolved) and the device's CU count, so every entry point that
+// depends on the query block (partial, combine, scratch size, the block
+// size query) sees the same one.
+sk::PartialKernel pick_partial(const sk_problem& p_in) {
+    sk_problem p = p_in;
+    if (p.split_kv == 0) p.split_kv = auto_split_kv(p_in);
     // Decode (every sequence at most one query row): the streaming kernel
     // where it exists for the head dims.
     if (p.max_seqlen_q == 1) {
         const sk::PartialKernel d = sk::find_partial_decode(p.dtype, p.head_dim_qk, p.head_dim_v);
         if (d.launch) return d;
     }
-    if (p.dtype == SK_BF16) return sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v);
-    if (p.dtype == SK_F16) return sk::find_partial_f16(p.head_dim_qk, p.head_dim_v);
+    if (p.dtype == SK_BF16 || p.dtype == SK_F16) {
+        // 256-row workgroups (one per CU, every tile loaded once for twice
+        // the rows) once there is at least one such item per CU; below that
+        // the 128-row kernel spreads the work over twice as many workgroups.
+        // Without a device (CU count unknown) the 128-row kernel.
+        const int cus = cu_count();
+        const bool two = cus > 0 && partial_work_items(p, 256) >= cus;
+        return p.dtype == SK_BF16 ? sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v, two)
+                                  : sk::find_partial_f16(p.head_dim_qk, p.head_dim_v, two);
+    }
     return sk::find_partial_f32(p.head_dim_qk, p.head_dim_v);
 }
 
@@ -358,7 +381,7 @@ static sk_status partial_impl(const sk_problem* p, const void* q, const void* k,
         return fail(SK_ERR_UNSUPPORTED, "K/V row strides above 2^24 elements are not supported");
 
     const int64_t n_tiles = (p->max_seqlen_q + kern.m_per_block - 1) / kern.m_per_block;
-    const int64_t n_work = n_tiles * p->num_heads * p->split_kv * (int64_t)p->batch;
+    const int64_t n_work = partial_work_items(*p, kern.m_per_block);
     if (n_work >= ((int64_t)1 << 31)) return fail(SK_ERR_UNSUPPORTED, "too many work items");
 
     sk::PartialArgs a;
