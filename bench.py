@@ -115,7 +115,7 @@ def write_traffic(fetch_dir: str, write_dir: str, path: str = TRAFFIC_FILE) -> d
     H, Sq, Sk, S = w.heads, w.sq[0], w.sk[0], w.split_kv
     algorithmic = Sq * H * w.d_qk * 2 + Sk * H * (w.d_qk + w.d_v) * 2 + S * H * Sq * (w.d_v + 1) * 4
     out = {
-        "kernel": "sk_attn_partial: partial_bf16_kernel<192,128> + merge_pieces_kernel<128,128>",
+        "kernel": "sk_attn_partial: partial_bf16_kernel<192,128> (256-row workgroups) + merge_pieces_kernel<256,128>",
         "workload": w.name,
         "kernel_source_sha256": kernel_source_hash(),
         "kernel_sources": PARTIAL_SOURCES,
@@ -738,8 +738,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
-            "kernel": "sk_attn_partial (partial_bf16_kernel<192,128>, then merge_pieces_kernel<128,128> for the "
-                      "last round's key pieces)",
+            "kernel": f"sk_attn_partial (partial_bf16_kernel<192,128> in {prob.m_per_block}-row workgroups, then "
+                      f"merge_pieces_kernel<{prob.m_per_block},128> for the last round's key pieces)",
             "kernel_ms": t_partial,
             "algorithmic_flop": flops,
             "algorithmic_bytes": partial_bytes,
