@@ -1,19 +1,19 @@
 // Split-KV partial attention, bf16 or f16 storage, 16-bit MFMA with f32
 // accumulation.
 //
-// Per (sequence, head, split, block of 128 query rows) the kernel computes the
-// partial output O_s and log-sum-exp L_s over the split's keys (rocmlirTriton
-// page "Recombine fully masked split-KV attention partials on the host":
-// Summary for the partials and the empty-split convention, "Per-row
-// valid-split counts" for the block's key partition).  The workload it is
+// Per (sequence, head, split, block of 128 or 256 query rows) the kernel
+// computes the partial output O_s and log-sum-exp L_s over the split's keys
+// (rocmlirTriton page "Recombine fully masked split-KV attention partials on
+// the host": Summary for the partials and the empty-split convention,
+// "Per-row valid-split counts" for the block's key partition).  The workload it is
 // tuned for is the long-context packed-varlen prefill of the aiter page
 // "[ASM][HIP][JIT][gfx942] Optimize long-context FMHA with split-KV"
 // (D_qk = 192, D_v = 128), re-designed for gfx950:
 //
 //  * 32 query rows per wave, in groups of 4 waves (one per SIMD).  GEMM0 is
-//    computed transposed, S^T = K Q^T,
-//    with v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and Q^T
-//    (kept in registers for the whole key loop) the B operand.  The
+//    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K
+//    (from LDS) is the A operand and Q^T (kept in registers for the whole key
+//    loop) the B operand.  The
 //    accumulator then gives every lane ONE query column and 16 keys, so the
 //    row max / row sum are in-lane reductions plus one exchange between the
 //    two half-waves.
