@@ -147,16 +147,18 @@ int64_t sk_rows(const sk_problem* p);
 /* The number of splits S_max every entry point uses for `p` (>= 1), or -1 if
  * `p` is invalid.  It is split_kv, or with split_kv = 0 the automatic choice
  * (aiter page, Technical Details: split only when the keys are long and the
- * query tiles alone do not fill the GPU), re-derived for this device:
- *   items = query blocks x heads, with blocks of the partial kernel chosen
- *           for `p` with split_kv = 1 (sk_partial_m_per_block: 128 or 256
- *           rows, or 1 for the decode kernel): batch x blocks of the longest
- *           sequence, or for a packed batch at most ceil(total_q / block) +
- *           B - 1
- *   slots = resident workgroups of that kernel on the device (2 per CU for
- *           the 128-row kernel, 1 for the 256-row one)
- *   S     = clamp(round(slots / items), 2, 8)  if max_seqlen_k >= 8192 and
- *           items <= slots, else 1.
+ * query tiles alone do not fill the GPU), re-derived for this device.  With
+ *   blocks(m) = query blocks of m rows: batch x blocks of the longest
+ *               sequence, or for a packed batch at most ceil(total_q / m) +
+ *               B - 1
+ * S = 1 if max_seqlen_k < 8192.  Otherwise, for 16-bit storage with an MFMA
+ * kernel (max_seqlen_q > 1 or head dims without a decode kernel), S is the
+ * smallest count in 1..7 with blocks(256) x heads x S >= the device's CU
+ * count (one item of the 256-row kernel per CU), else 8.  For the decode
+ * kernel (one-row sequences), with
+ *   items = blocks(1) x heads: one item per (sequence, head)
+ *   slots = the decode kernel's resident workgroups on the device
+ *   S     = clamp(round(slots / items), 2, 8)  if items <= slots, else 1.
  * The key threshold is the explicit 8192 of that page's contract (its review
  * notes a tile-rounded form that also split 8161..8191 keys).  f32 problems
  * and head dims without a 16-bit kernel stay unsplit.  The result depends on
@@ -179,9 +181,9 @@ int64_t sk_partial_scratch_bytes(const sk_problem* p);
  * page, the paragraph on conservative counts), so the partials depend on it.
  * 1 for a 16-bit problem with max_seqlen_q = 1 and head dims 64/64 or
  * 128/128 (the decode kernel), 64 for f32.  Other 16-bit problems: 256 when
- * the partial grid at 256-row blocks, ceil(max_seqlen_q / 256) x num_heads x
- * split_kv (resolved) x batch items, has at least one item per CU of the
- * current device, else 128 (and 128 when no device is present).  Like the
+ * blocks(256) x num_heads x split_kv (resolved; blocks() as in sk_split_kv)
+ * reaches the CU count of the current device, one item per CU, else 128 (and
+ * 128 when no device is present).  Like the
  * automatic split count, the value depends on the current device, so every
  * call for one problem must see the same device current. */
 int32_t sk_partial_m_per_block(const sk_problem* p);

@@ -118,6 +118,15 @@ int64_t partial_work_items(const sk_problem& p, int64_t m_per_block) {
     return (p.max_seqlen_q + m_per_block - 1) / m_per_block * p.num_heads * p.split_kv * (int64_t)p.batch;
 }
 
+// Query blocks of m_per_block rows that hold rows: batch x blocks of the
+// longest sequence, and for a packed batch at most ceil(total_q / block) +
+// B - 1 (the host knows only these sizes; the lengths live on the device).
+int64_t query_blocks(const sk_problem& p, int64_t m_per_block) {
+    int64_t t = (int64_t)p.batch * ((p.max_seqlen_q + m_per_block - 1) / m_per_block);
+    if (p.cu_seqlens_q) t = std::min(t, ((int64_t)p.total_q + m_per_block - 1) / m_per_block + p.batch - 1);
+    return t;
+}
+
 // The partial kernel of a problem: a function of the problem (its split
 // count resolved) and the device's CU count, so every entry point that
 // depends on the query block (partial, combine, scratch size, the block
@@ -137,7 +146,7 @@ sk::PartialKernel pick_partial(const sk_problem& p_in) {
         // the 128-row kernel spreads the work over twice as many workgroups.
         // Without a device (CU count unknown) the 128-row kernel.
         const int cus = cu_count();
-        const bool two = cus > 0 && partial_work_items(p, 256) >= cus;
+        const bool two = cus > 0 && query_blocks(p, 256) * p.num_heads * p.split_kv >= cus;
         return p.dtype == SK_BF16 ? sk::find_partial_bf16(p.head_dim_qk, p.head_dim_v, two)
                                   : sk::find_partial_f16(p.head_dim_qk, p.head_dim_v, two);
     }
@@ -208,11 +217,20 @@ int32_t auto_split_kv(const sk_problem& p) {
     q.split_kv = 1;
     const sk::PartialKernel k = pick_partial(q);
     if (!k.launch || p.dtype == SK_F32) return 1;
+    // 16-bit MFMA kernels: the fewest splits that give the 256-row kernel
+    // one item per CU (the last round's remainder runs as key pieces), at
+    // most 8.
+    if (k.m_per_block > 1) {
+        const int64_t cus = cu_count();
+        if (cus <= 0) return 1;
+        const int64_t per_split = query_blocks(p, 256) * p.num_heads;
+        for (int64_t s = 1; s < kMaxAutoSplits; ++s)
+            if (per_split * s >= cus) return (int32_t)s;
+        return (int32_t)kMaxAutoSplits;
+    }
+    // The decode kernel: about one item per resident workgroup.
     const int64_t slots = partial_slots(k);
-    const int64_t mpb = k.m_per_block;
-    int64_t tiles = (int64_t)p.batch * ((p.max_seqlen_q + mpb - 1) / mpb);
-    if (p.cu_seqlens_q) tiles = std::min(tiles, ((int64_t)p.total_q + mpb - 1) / mpb + p.batch - 1);
-    const int64_t items = tiles * p.num_heads;
+    const int64_t items = query_blocks(p, k.m_per_block) * p.num_heads;
     if (slots <= 0 || items <= 0 || items > slots) return 1;
     return (int32_t)std::clamp((slots + items / 2) / items, (int64_t)2, kMaxAutoSplits);
 }

@@ -194,26 +194,29 @@ def test_tail_split_all_rows(w):
 
 
 def test_automatic_split_count_both_sides_of_the_thresholds():
-    """split_kv = 0: unsplit below 8192 keys or when the query tiles alone
-    fill the GPU, else clamp(round(slots / items), 2, 8) splits."""
+    """split_kv = 0: unsplit below 8192 keys; above, the fewest splits (up to
+    8) that give the 256-row kernel one item per CU, which then runs it."""
     from split_kv_attention_amd import attention
 
-    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count  # two workgroups per CU
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
 
-    def auto(sq, sk, dtype="bf16"):
-        w = _shrink(workloads.LONG_PREFILL, sq=(sq,), sk=(sk,), split_kv=0, dtype=dtype)
+    def auto(sq, sk, dtype="bf16", d=(192, 128)):
+        w = _shrink(workloads.LONG_PREFILL, sq=(sq,), sk=(sk,), split_kv=0, dtype=dtype, d_qk=d[0], d_v=d[1])
         inputs = workloads.make_inputs(w, DEV, seed=0)
         prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
-        return prob.split_kv
+        return prob.split_kv, prob.m_per_block
 
-    def rule(items):
-        return max(2, min(8, (slots + items // 2) // items)) if items <= slots else 1
+    def rule(sq, heads=12):
+        per_split = -(-sq // 256) * heads  # 256-row items per split
+        return next((s for s in range(1, 8) if per_split * s >= cus), 8)
 
-    assert auto(1024, 8191) == 1  # one key below the threshold (the page's tile-rounded form split here)
-    assert auto(1024, 8192) == rule(12 * 8) > 1
-    assert auto(4096, 42700) == rule(12 * 32)
-    assert auto(8192, 16384) == (rule(12 * 64) if 12 * 64 <= slots else 1)
-    assert auto(1024, 8192, dtype="f32") == 1  # no bf16 MFMA kernel contract
+    assert auto(1024, 8191) == (1, 128)  # one key below the threshold (the page's tile-rounded form split here)
+    assert auto(1024, 8192) == (rule(1024), 256) and rule(1024) > 1
+    assert auto(2048, 42700) == (rule(2048), 256)
+    assert auto(4096, 42700) == (rule(4096), 256)
+    assert auto(8192, 16384) == (rule(8192), 256)
+    assert auto(256, 8192) == (8, 128)  # too few rows to fill the CUs even at 8 splits
+    assert auto(1024, 8192, dtype="f32", d=(64, 64)) == (1, 64)  # the f32 kernel: unsplit
 
 
 def test_automatic_split_end_to_end():

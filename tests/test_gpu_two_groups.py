@@ -25,8 +25,16 @@ pytestmark = pytest.mark.gpu
 CUS = 256  # MI355X compute units: one 256-row item per CU or more
 
 
+def _blocks(sq, packed: bool) -> int:
+    """256-row query blocks as the library counts them from the sizes the
+    host knows: B x blocks of the longest sequence, for a packed batch at
+    most ceil(total rows / 256) + B - 1."""
+    dense = -(-max(sq) // 256) * len(sq)
+    return min(dense, -(-sum(sq) // 256) + len(sq) - 1) if packed else dense
+
+
 def _items(w: Workload) -> int:
-    return -(-max(w.sq) // 256) * w.heads * w.split_kv * len(w.sq)
+    return _blocks(w.sq, w.packed) * w.heads * w.split_kv
 
 
 CASES = [
@@ -67,8 +75,7 @@ def _draw(seed: int) -> Workload:
     offsets = tuple(int(sk[b] - sq[b] + rng.integers(-64, 65)) for b in range(B)) if mask == "prefix_causal" else None
     last_valid = tuple(int(rng.integers(-1, max(sk[b], 1))) for b in range(B)) if rng.random() < 0.3 else None
     window = int(rng.integers(0, 600)) if rng.random() < 0.3 else -1
-    blocks = -(-max(sq) // 256)
-    heads = max(1, -(-CUS // (blocks * split_kv * B)))
+    heads = max(1, -(-CUS // (_blocks(sq, packed) * split_kv)))
     name = (f"two_groups_rand{seed}_{dtype}_{'packed' if packed else 'dense'}_B{B}_H{heads}_D{d_qk}x{d_v}_"
             f"S{split_kv}_{mask}{'_lv' if last_valid else ''}{f'_w{window}' if window >= 0 else ''}")
     return Workload(name, heads=heads, sq=tuple(sq), sk=tuple(sk), d_qk=d_qk, d_v=d_v, split_kv=split_kv,
