@@ -3,8 +3,8 @@
 The no-alloc variant runs the same kernels with the library's own static
 scratch for the last round's key pieces instead of the caller's buffer, so
 its partials must equal sk_attn_partial's with a caller-allocated scratch
-bit for bit.  Two calls in a row, the second on a smaller problem, both of
-which use the key pieces (each differs from a run without scratch, where
+bit for bit.  Calls in a row, each on a smaller problem than the last, all
+of which use the key pieces (each differs from a run without scratch, where
 every item runs whole); the merged output of each is also checked against
 the oracle.
 """
@@ -19,9 +19,13 @@ from split_kv_attention_amd import _lib, attention, workloads
 
 pytestmark = pytest.mark.gpu
 
-# Both shapes leave a partial last round of workgroups whose items are cut
-# into key pieces (16+ key tiles per split).
+# Every shape leaves a partial last round of workgroups whose items are cut
+# into key pieces (16+ key tiles per split).  The first has 16 x 17 = 272
+# items of 256 rows, enough for the 256-row kernel on a 256-CU device (the
+# last 16 run as pieces); the others run the 128-row kernel.
 CASES = [
+    dataclasses.replace(workloads.LONG_PREFILL, name="noalloc_H16_Sq200_Sk17408_S17", heads=16, sq=(200,),
+                        sk=(17 * 1024,), split_kv=17),
     dataclasses.replace(workloads.LONG_PREFILL, name="noalloc_H12_Sq512_Sk6000_S3", sq=(512,), sk=(6000,)),
     dataclasses.replace(workloads.LONG_PREFILL, name="noalloc_H8_Sq256_Sk4000_S3", heads=8, sq=(256,), sk=(4000,)),
 ]
@@ -55,6 +59,7 @@ def test_noalloc_matches_partial_on_two_calls(order):
         inputs = workloads.make_inputs(w, DEV, seed=11)
         prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
         assert prob.c.partial_scratch and _lib.sk_partial_scratch_bytes(prob.c) > 0
+        log(f"  {prob.m_per_block}-row blocks")
         ref = _partials(prob, inputs, _lib.sk_attn_partial, scratch=True)
         got = _partials(prob, inputs, _lib.sk_attn_partial_noalloc, scratch=True)
         whole = _partials(prob, inputs, _lib.sk_attn_partial, scratch=False)
@@ -69,7 +74,7 @@ def test_noalloc_matches_partial_on_two_calls(order):
 
 
 def test_noalloc_ignores_the_callers_scratch_and_rejects_bad_arguments():
-    w = CASES[1]
+    w = CASES[-1]
     inputs = workloads.make_inputs(w, DEV, seed=12)
     prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
     ref = _partials(prob, inputs, _lib.sk_attn_partial, scratch=True)
