@@ -5,18 +5,17 @@
 // computes the partial output O_s and log-sum-exp L_s over the split's keys
 // (rocmlirTriton page "Recombine fully masked split-KV attention partials on
 // the host": Summary for the partials and the empty-split convention,
-// "Per-row valid-split counts" for the block's key partition).  The workload it is
-// tuned for is the long-context packed-varlen prefill of the aiter page
+// "Per-row valid-split counts" for the block's key partition).  The workload
+// it is tuned for is the long-context packed-varlen prefill of the aiter page
 // "[ASM][HIP][JIT][gfx942] Optimize long-context FMHA with split-KV"
 // (D_qk = 192, D_v = 128), re-designed for gfx950:
 //
 //  * 32 query rows per wave, in groups of 4 waves (one per SIMD).  GEMM0 is
 //    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K
 //    (from LDS) is the A operand and Q^T (kept in registers for the whole key
-//    loop) the B operand.  The
-//    accumulator then gives every lane ONE query column and 16 keys, so the
-//    row max / row sum are in-lane reductions plus one exchange between the
-//    two half-waves.
+//    loop) the B operand.  The accumulator then gives every lane ONE query
+//    column and 16 keys, so the row max / row sum are in-lane reductions plus
+//    one exchange between the two half-waves.
 //  * The same accumulator layout is exactly the B operand layout (key-major,
 //    query column per lane) GEMM1 needs for O^T = V^T P^T, so P never leaves
 //    registers: it is rounded to bf16 in place.  V stays row-major in LDS and
@@ -457,14 +456,14 @@ void partial_bf16_kernel(PartialArgs a) {
         mma_step(xb, pf[1][1]);
     };
 
-    // Pipeline.  Iteration i: the weights of tile i from its scores; GEMM0(i+1)
-    // from K slot (i+1)%2 into the same score registers, with the DMA of
-    // K(i+2) -> K slot i%2 and V(i+1) -> the V slot after tile i's spread
-    // over its steps; GEMM1(i); then tile i+1's mask / max update.  Every
-    // wave passes one barrier per iteration: the first group after GEMM1(i),
-    // the second before it.  The loads a barrier covers were issued before it
-    // by every wave (in GEMM0), and a slot is refilled only after the
-    // barrier that follows its last reader: K(i) is last read by GEMM0(i)
+    // Pipeline.  Iteration i: the weights of tile i from its scores;
+    // GEMM0(i+1) from K slot (i+1)%2 into the same score registers, with the
+    // DMA of K(i+2) into K slot i%2 and of V(i+1) into the V slot after tile
+    // i's spread over its steps; GEMM1(i); then tile i+1's mask / max update.
+    // Every wave passes one barrier per iteration: the first group after
+    // GEMM1(i), the second before it.  The loads a barrier covers were issued
+    // before it by every wave (in GEMM0), and a slot is refilled only after
+    // the barrier that follows its last reader: K(i) is last read by GEMM0(i)
     // in iteration i - 1; V(i - 2) by the second group's GEMM1(i - 2), which
     // runs between the barriers of iterations i - 2 and i - 1.
     const int ntiles = ks < ke ? (ke - ks + kBN - 1) / kBN : 0;
