@@ -95,3 +95,31 @@ def test_two_group_kernel_all_rows(w):
     assert prob.m_per_block == 256, "the library picked the 128-row kernel"
     st = compare(w, inputs, prob, res, label=w.name)
     log(f"  {st}")
+
+
+def _choice(w: Workload) -> int:
+    from split_kv_attention_amd import attention
+
+    inputs = workloads.make_inputs(w, "cuda", seed=0)
+    prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
+    return prob.m_per_block
+
+
+def test_kernel_choice_at_one_item_per_cu():
+    """The 256-row kernel from exactly one 256-row item per CU, the 128-row
+    one below; a packed batch counts at most ceil(total rows / 256) + B - 1
+    blocks (here 3 where the longest sequence alone would give 4)."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dense = Workload("choice_dense", heads=cus, sq=(100,), sk=(300,), d_qk=64, d_v=64, split_kv=1, n_per_block=64)
+    assert _choice(dense) == 256
+    assert _choice(dataclasses.replace(dense, heads=cus - 1)) == 128
+    packed = Workload("choice_packed", heads=-(-cus // 3), sq=(300, 1), sk=(300, 300), d_qk=64, d_v=64, split_kv=1,
+                      n_per_block=64, packed=True)
+    assert _blocks(packed.sq, True) == 3 and _items(packed) >= cus
+    assert _choice(packed) == 256
+    assert _choice(dataclasses.replace(packed, heads=(cus - 1) // 3)) == 128
+    for w in (dense, dataclasses.replace(dense, heads=cus - 1), packed):
+        inputs, prob, res = run_gpu(w, seed=62)
+        compare(w, inputs, prob, res, label=w.name)
