@@ -90,6 +90,11 @@ CASES = [
                                    last_valid_per_seq=(499, 69, 1499, 2999))),
     ("padded", dataclasses.replace(workloads.DECODE_BF16, name="layout_padded_decode_packed", packed=True,
                                    sq=(1, 1, 0, 1), sk=(900, 2049, 10, 0), heads=3, d_qk=64, d_v=64, split_kv=5)),
+    # sized for the 256-row kernel (at least one 256-row item per CU on MI355X)
+    ("bshd", dataclasses.replace(workloads.CAUSAL_BF16, name="layout_bshd_causal_256rows", sq=(300, 300),
+                                 sk=(2500, 2500), heads=16, split_kv=4)),
+    ("padded", dataclasses.replace(workloads.LONG_PREFILL, name="layout_padded_prefill_256rows", sq=(300,),
+                                   sk=(3000,), heads=16, split_kv=8)),
 ]
 
 
@@ -97,6 +102,8 @@ CASES = [
 def test_strided_layouts_forward_all_rows(layout, w):
     log(f"layout {w.name}")
     inputs, prob, res = _run(w, layout, seed=23)
+    if w.name.endswith("_256rows"):
+        assert prob.m_per_block == 256
     st = compare(w, inputs, prob, res, label=w.name)
     log(f"  {st}")
 
