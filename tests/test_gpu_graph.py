@@ -25,6 +25,9 @@ CASES = [
                         prefix_offset_per_seq=(370, 69, 1243, 2936), last_valid_per_seq=(499, 69, 1499, 2999)),
     dataclasses.replace(workloads.LONG_PREFILL, name="graph_tail_split_H2_Sq256_Sk8192", heads=2, sq=(256,),
                         sk=(8192,), split_kv=2),
+    # the 256-row kernel (288 items of 256 rows) with its last 32 items as key pieces
+    dataclasses.replace(workloads.LONG_PREFILL, name="graph_256rows_pieces_H16_Sq300_Sk9216_S9", heads=16,
+                        sq=(300,), sk=(9216,), split_kv=9),
 ]
 
 
@@ -40,6 +43,8 @@ def test_forward_graph_replays_match_eager(w):
     inputs = workloads.make_inputs(w, DEV, 21)
     prob = attention.build_problem(inputs["q"], inputs["k"], inputs["v"], **workloads.problem_kwargs(w, inputs))
     bufs = attention.alloc_outputs(prob, inputs["q"], inputs["v"])  # counts, o_part, lse_part, out, lse_out
+    if "256rows" in w.name:
+        assert prob.m_per_block == 256
     _eager(prob, inputs, bufs)  # warm-up: per-device caches are filled outside the capture
 
     graph = torch.cuda.CUDAGraph()
