@@ -30,6 +30,9 @@ CASES = [
                         last_valid_kv_index=1400),
     dataclasses.replace(workloads.DECODE_BF16, name="c_client_decode_B8_H4_Sk3000", sq=(1,) * 8, sk=(3000,) * 8,
                         heads=4),
+    # 256 items of 256 rows: the 256-row kernel on a 256-CU device
+    dataclasses.replace(workloads.CAUSAL_BF16, name="c_client_causal_256rows_B2_H16_Sq300_Sk2500", sq=(300, 300),
+                        sk=(2500, 2500), heads=16),
 ]
 
 

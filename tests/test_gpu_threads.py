@@ -2,9 +2,9 @@
 through the C ABI).
 
 The library keeps no per-call state outside the arguments: its per-device
-caches are atomics and its error message is per thread.  Four threads run
+caches are atomics and its error message is per thread.  Five threads run
 different workloads, each on its own stream, several times over, while a
-fifth thread makes calls that fail argument checks.  Every thread's last
+sixth thread makes calls that fail argument checks.  Every thread's last
 results must equal, bit for bit, a run of the same workload alone, and each
 thread must read its own error message.
 """
@@ -29,6 +29,9 @@ CASES = [
                         dtype="f16"),
     dataclasses.replace(workloads.DECODE_BF16, name="threads_decode_B8_H4_Sk3000", sq=(1,) * 8, sk=(3000,) * 8,
                         heads=4),
+    # the 256-row kernel, its last round as key pieces
+    dataclasses.replace(workloads.LONG_PREFILL, name="threads_256rows_pieces_H16_Sq300_Sk9216_S9", heads=16,
+                        sq=(300,), sk=(9216,), split_kv=9),
 ]
 ROUNDS = 6
 
