@@ -123,3 +123,45 @@ def test_kernel_choice_at_one_item_per_cu():
     for w in (dense, dataclasses.replace(dense, heads=cus - 1), packed):
         inputs, prob, res = run_gpu(w, seed=62)
         compare(w, inputs, prob, res, label=w.name)
+
+
+def test_block_size_and_automatic_split_follow_the_documented_rules():
+    """Host queries only (no kernel runs), over seeded random shapes: the
+    block size is 256 exactly when the 256-row item count reaches the CU
+    count, and split_kv = 0 resolves to the fewest splits (at most 8) that
+    reach it, for problems with at least 8192 keys and more than one row."""
+    import torch
+
+    from split_kv_attention_amd import _lib
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(8900)
+    for _ in range(400):
+        packed = bool(rng.random() < 0.5)
+        B = int(rng.integers(1, 9))
+        sq = [int(x) for x in rng.integers(2, 2049, B)]
+        if not packed:
+            sq = [max(sq)] * B
+        sk = int(rng.choice([4096, 8191, 8192, 20000, 42700]))
+        heads = int(rng.integers(1, 33))
+        split = int(rng.integers(0, 13))
+        dtype = "bf16" if rng.random() < 0.7 else "f16"
+        w = Workload("rules", heads=heads, sq=tuple(sq), sk=(sk,) * B, d_qk=128, d_v=128, split_kv=split,
+                     n_per_block=64, packed=packed, dtype=dtype)
+        c = _lib.SkProblem()
+        c.batch, c.num_heads, c.max_seqlen_q, c.max_seqlen_k = B, heads, max(sq), sk
+        c.head_dim_qk = c.head_dim_v = 128
+        c.split_kv, c.n_per_block = split, 64
+        c.dtype = c.out_dtype = _lib.SK_BF16 if dtype == "bf16" else _lib.SK_F16
+        c.softmax_scale = 0.1
+        c.window_left = -1
+        c.last_valid_kv_index = -1
+        if packed:
+            c.cu_seqlens_q = 1 << 20  # never dereferenced by these host queries
+            c.total_q = sum(sq)
+        per_split = _blocks(sq, packed) * heads
+        s_exp = split
+        if split == 0:
+            s_exp = 1 if sk < 8192 else next((s for s in range(1, 8) if per_split * s >= cus), 8)
+        assert _lib.sk_split_kv(c) == s_exp, (w, s_exp)
+        assert _lib.sk_partial_m_per_block(c) == (256 if per_split * s_exp >= cus else 128), (w, s_exp)
