@@ -21,10 +21,11 @@
 //    registers: it is rounded to bf16 in place.  V stays row-major in LDS and
 //    its A operand is read with ds_read_b64_tr_b16, which hands each lane four
 //    keys of one value column.
-//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-//    register staging), double-buffered: the next tile streams in while the
-//    current one is multiplied, with one barrier per tile.  16-byte chunks are
-//    XOR-swizzled by row so both operand reads are bank-conflict free.
+//  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
+//    no register staging), in two K and two or three V slots: the next tile
+//    streams in while the current one is multiplied, with one barrier per
+//    tile.  16-byte chunks are XOR-swizzled by row so both operand reads are
+//    bank-conflict free.
 //  * Large problems take two groups (8 waves, 256 rows, one workgroup per
 //    CU): every tile is loaded once for twice the rows.  The second group
 //    passes the tile's barrier between its GEMM0 and GEMM1, the first after
@@ -185,9 +186,9 @@ void partial_bf16_kernel(PartialArgs a) {
     const float cl2 = a.scale_log2;
 
     // Direct HBM -> LDS tile loads (buffer_load ... lds).  Load i of this
-    // thread fills LDS chunk P = 256 i + tid of the tile (a wave covers 64
-    // consecutive chunks); the chunk holds row P / CH and, after the swizzle,
-    // column chunk c of that row.  The byte offset from the tile's first key
+    // thread fills LDS chunk P = kThreads i + tid of the tile (a wave covers
+    // 64 consecutive chunks); the chunk holds row P / CH and, after the
+    // swizzle, column chunk c of that row.  The byte offset from the tile's first key
     // is the same for every tile.
     uint32_t k_off[C::K_LOADS], v_off[C::V_LOADS];
 #pragma unroll
